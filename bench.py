@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Router benchmark on one MI355X: quantize + gate GEMM + top-k per step.
+
+A step is one router call: router_quantize on the step's activations, then
+router_gate_topk (gate projection and the six-step epilogue). The default
+workload is the decode router: T=1, D=7168, E=256, k=8, with 61 independent
+layer sets (token, NVFP4 gate weights, bias) cycled call by call, inputs
+resident in HBM before timing. Gate weights are quantized once at load time
+by the library itself (untimed), as the pages do for bf16 weights.
+
+Steps are replayed from a HIP graph (the decode loop of the pages is
+graph-captured), with the eager rate reported alongside. Kernel durations
+for the roofline come from HIP events around each launch on the launch
+stream. The CPU baseline is the oracle, timed on a bounded sample.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "router tokens/s (quant+gate GEMM+top-k) D=7168,E=256,k=8; µs/call at T=1"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gate_bytes(c):
+    """Algorithmic bytes of one gate launch: W codes+scales, x codes+scales, bias, outputs."""
+    return c.E * c.D * 9 // 16 + c.T * c.D * 9 // 16 + 4 * c.E + 8 * c.T * c.k
+
+
+def quant_bytes(c):
+    """Algorithmic bytes of one quantize call: x read once (single pass) or twice, codes+scales written."""
+    reads = 2 if c.T * c.D // 16 > 2048 else 1
+    return reads * 2 * c.T * c.D + c.T * c.D * 9 // 16 + 4
+
+
+def gate_flops(c):
+    return 2 * c.T * c.E * c.D
+
+
+def cpu_baseline(cfg, seconds):
+    """The oracle as it stands, one router call after another on the host, for about `seconds`."""
+    from nvfp4_block_scaled_06_amd import workloads as wl
+    from oracle import quant_ref, router_ref
+
+    c = wl.CONFIGS[cfg]
+    nlayers = min(c.layers, 4)
+    wq = [quant_ref.quantize_ref(wl.make_w(cfg, l)) for l in range(nlayers)]  # load time, untimed
+    bias = [wl.make_bias(cfg, l) for l in range(nlayers)]
+    if c.T * c.D > 64 * 7168:
+        rows = 64
+        xs = [wl.make_x(cfg)[:rows]]
+    else:
+        rows = c.T
+        xs = [wl.make_x(cfg, l) for l in range(nlayers)]
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        l = calls % nlayers
+        xq = quant_ref.quantize_ref(xs[l % len(xs)])
+        L, _ = router_ref.logits_ref(*xq, *wq[l])
+        router_ref.route_ref(L, bias[l], c.k, c.routed_scale)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    return {"value": calls * rows / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{calls} oracle router calls of {rows} token(s) cycling {nlayers} of the layer sets "
+                      f"({el:.1f} s; numpy float64, weights quantized beforehand)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", type=int, default=2, help="router shape 1..5 (2 = decode T=1)")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the router path is single-GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from nvfp4_block_scaled_06_amd import router as rt
+    from nvfp4_block_scaled_06_amd import workloads as wl
+
+    rt.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = wl.CONFIGS[args.config]
+    K, W = args.steps, args.warmup
+    log(f"workload cfg {c.cfg} {c.name}: T={c.T} D={c.D} E={c.E} k={c.k} layers={c.layers}")
+
+    ws = rt.Workspace.for_shapes([(c.T, c.D, c.E, c.k), (c.E, c.D, c.E, c.k)], dev)
+    wq, bias, xs = [], [], []
+    for l in range(c.layers):
+        w = torch.from_numpy(wl.make_w(c.cfg, l).view(np.int16)).to(dev)
+        wq.append(rt.quantize(w, ws))  # load time
+        del w
+        bias.append(torch.from_numpy(wl.make_bias(c.cfg, l)).to(dev))
+        xs.append(torch.from_numpy(wl.make_x(c.cfg, l).view(np.int16)).to(dev))
+    xq = rt.empty_nvfp4(c.T, c.D, dev)
+    out = (torch.empty((c.T, c.k), dtype=torch.int32, device=dev),
+           torch.empty((c.T, c.k), dtype=torch.float32, device=dev), None)
+    torch.cuda.synchronize()
+    log("inputs resident")
+
+    def step(i):
+        l = i % c.layers
+        rt.quantize(xs[l], ws, out=xq)
+        rt.gate_topk(xq, wq[l], bias[l], c.k, c.routed_scale, ws, out=out)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Eager rate.
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(W + i)
+    torch.cuda.synchronize()
+    eager_s = time.perf_counter() - t0
+    log(f"eager: {eager_s / K * 1e6:.2f} us/call")
+
+    graph_s = None
+    if not args.eager:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(K):
+                    step(W + i)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()  # untimed warm replay
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        graph_s = time.perf_counter() - t0
+        log(f"graph: {graph_s / K * 1e6:.2f} us/call")
+    timed_s = eager_s if graph_s is None else graph_s
+
+    # Per-kernel durations with events on the launch stream (eager launches).
+    nk = min(K, 500)
+    cur = torch.cuda.current_stream()
+    evq = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
+    evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
+    for i in range(nk):
+        l = (W + i) % c.layers
+        evq[i][0].record(cur)
+        rt.quantize(xs[l], ws, out=xq)
+        evq[i][1].record(cur)
+        evg[i][0].record(cur)
+        rt.gate_topk(xq, wq[l], bias[l], c.k, c.routed_scale, ws, out=out)
+        evg[i][1].record(cur)
+    torch.cuda.synchronize()
+    tq = float(np.mean([a.elapsed_time(b) for a, b in evq])) * 1e-3
+    tg = float(np.mean([a.elapsed_time(b) for a, b in evg])) * 1e-3
+    log(f"kernel times: quantize {tq * 1e6:.2f} us, gate {tg * 1e6:.2f} us")
+
+    if c.T >= 4096:
+        achieved = gate_flops(c) / tg / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None, "kernel": "gate (fused MFMA + top-k)"}
+    else:
+        achieved = gate_bytes(c) / tg / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gate (split GEMV-MFMA + top-k)"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(c.cfg, args.cpu_seconds)
+
+    ms = timed_s / K * 1e3
+    line = {
+        "metric": METRIC,
+        "value": c.T * K / timed_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 operands, f16 MFMA, f32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{c.name} router T={c.T} D={c.D} E={c.E} k={c.k}, {c.layers} layer set(s) cycled",
+            "T": c.T, "D": c.D, "E": c.E, "k": c.k,
+            "launch": "eager" if graph_s is None else "hipgraph",
+            "us_per_call": ms * 1e3,
+            "eager_us_per_call": eager_s / K * 1e6,
+            "quantize_kernel_us": tq * 1e6,
+            "gate_kernel_us": tg * 1e6,
+            "parallelism": "single GPU",
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

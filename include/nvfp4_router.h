@@ -1,0 +1,129 @@
+/*
+ * nvfp4_router.h -- C ABI of the MI355X (gfx950) NVFP4 dense-MoE router library
+ * (libnvfp4_router.so).
+ *
+ * The path: runtime NVFP4 quantization of the activations, the block-scaled
+ * gate projection to per-expert logits, and the fused six-step routing
+ * epilogue. Sources are three commit pages of the nvfp4-megamoe-kernel
+ * repository:
+ *   - commit 04cf8ca8, dsv4/layers/router.py: runtime global scale
+ *     gsa = max|x| / (6 * 448), the E4M3 block-scale ceiling of 448, the
+ *     NVFP4 gate GEMM and the fused-router dispatch order;
+ *   - commit e0f60b9f, dsv4/kernels/router/__init__.py: the six-step
+ *     single-pass activation/top-k epilogue after the gate GEMM;
+ *   - commit df05289d, dsv4/layers/grouped_linear.py: one flattened
+ *     quantize launch with a device-only global scale, no host syncs and
+ *     caller-owned pre-allocated buffers.
+ * The NVFP4 format fixes the rest: 16-element blocks along the contraction
+ * axis, E4M3 (OCP "FN", max 448) block scales, E2M1 element codes, one fp32
+ * per-tensor global scale.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; tensors
+ *     are dense and row-major. The library allocates nothing and keeps no
+ *     per-call state; it only enqueues work on `stream` (a hipStream_t, NULL
+ *     for the default stream) and never synchronizes or copies to the host,
+ *     so calls may be captured in a HIP graph.
+ *   - A negative return value means the arguments were rejected on the host
+ *     and nothing was enqueued, except ROUTER_EHIP (a launch failed).
+ *   - Non-finite input values are a precondition violation: they make the
+ *     global scale non-finite (the device-visible error flag) and leave the
+ *     other outputs unspecified.
+ *   - Calls that share one workspace must not overlap in time (enqueue them
+ *     on one stream).
+ */
+#ifndef NVFP4_ROUTER_H
+#define NVFP4_ROUTER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROUTER_OK 0
+#define ROUTER_EINVAL (-1)       /* bad shape, null or misaligned pointer, workspace too small */
+#define ROUTER_EUNSUPPORTED (-2) /* a documented size limit is exceeded */
+#define ROUTER_EHIP (-3)         /* a kernel launch reported an error */
+
+#define ROUTER_MAX_EXPERTS 512
+#define ROUTER_MAX_TOPK 32
+
+/*
+ * Bytes of workspace that router_quantize and router_gate_topk need for a
+ * call with these sizes (rows = T tokens, D hidden, E experts, k chosen).
+ * One workspace sized by this function serves both calls.
+ *
+ * The first 256 bytes hold arrival counters that must be zero before the
+ * first call (allocate zero-filled memory or call router_workspace_init);
+ * every call leaves them zero again. Returns 0 for invalid sizes.
+ */
+size_t router_workspace_bytes(int64_t T, int64_t D, int64_t E, int64_t k);
+
+/*
+ * Zero-fills `bytes` of `workspace` on `stream` with a kernel (no memset
+ * node, so it may be captured). Needed once per workspace allocation.
+ */
+int router_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/*
+ * Runtime NVFP4 quantization of x (the flattened single-launch quantizer
+ * with a device-only global scale: commit df05289d,
+ * dsv4/layers/grouped_linear.py; the scale rule: commit 04cf8ca8,
+ * dsv4/layers/router.py, runtime-gsa paragraph).
+ *
+ *   x            [rows, D] bf16 bit patterns, 16-byte aligned.
+ *   rows, D      rows >= 0, D >= 16, D % 16 == 0.
+ *   gsa_override NULL: gsa = fp32(max|x|) / 2688 (one IEEE fp32 division).
+ *                Else a device fp32 scalar used as gsa instead (reproduces a
+ *                static scale; must be >= 0 and finite).
+ *   codes        [rows, D/2] out: E2M1 codes, element 2i in the low nibble of
+ *                byte i; each code is the E2M1 value nearest to
+ *                |x| / (gsa * S) (ties to even, saturating at 6) with the
+ *                sign bit of x. 8-byte aligned.
+ *   scales       [rows, D/16] out: E4M3FN bytes; each is the E4M3 value nearest
+ *                to bmax / (6 * gsa) over its 16-element block (ties to even,
+ *                saturating at 448).
+ *   gsa_out      [1] out: the global scale used (device fp32).
+ * gsa == 0 gives zero scale bytes and sign-only codes. Every rounding is
+ * exact (identical to the infinitely precise quotient's).
+ *
+ * Also used at load time on bf16 gate weights [E, D] (their gsa is gsw).
+ */
+int router_quantize(const void* x, int64_t rows, int64_t D, const float* gsa_override, uint8_t* codes,
+                    uint8_t* scales, float* gsa_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gate projection plus the fused routing epilogue (gate GEMM on NVFP4
+ * operands: commit 04cf8ca8, dsv4/layers/router.py; six-step epilogue:
+ * commit e0f60b9f, dsv4/kernels/router/__init__.py).
+ *
+ *   x_codes, x_scales, gsa   router_quantize outputs for x [T, D].
+ *   w_codes, w_scales, gsw   the gate weights in the same format, [E, D/2],
+ *                            [E, D/16] and a device fp32 scalar.
+ *   bias                     [E] fp32 selection bias.
+ *   routed_scale             host fp32 factor applied after renormalization.
+ *   T, D, E, k               T >= 0; D % 32 == 0; 1 <= E <= 512;
+ *                            1 <= k <= min(E, 32).
+ *   topk_idx                 [T, k] int32 out: experts by descending
+ *                            s + bias, an exact tie going to the lower index.
+ *   topk_w                   [T, k] fp32 out: routed_scale * s / sum(s) over
+ *                            the chosen experts, s = sigmoid(logit).
+ *   logits_out               NULL, or [T, E] fp32 out: the logits
+ *                            gsa * gsw * sum_d xhat * what (fp32 accumulation).
+ * Code and scale pointers must be 16- and 2-byte aligned.
+ */
+int router_gate_topk(const uint8_t* x_codes, const uint8_t* x_scales, const float* gsa, const uint8_t* w_codes,
+                     const uint8_t* w_scales, const float* gsw, const float* bias, float routed_scale, int64_t T,
+                     int64_t D, int64_t E, int64_t k, int32_t* topk_idx, float* topk_w, float* logits_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* router_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_ROUTER_H */

@@ -1,0 +1,189 @@
+// Runtime NVFP4 quantization of a bf16 tensor (gfx950).
+//
+// One global scale per call, computed on the device (commit df05289d,
+// dsv4/layers/grouped_linear.py: one flattened quantize launch, no host
+// sync for gsa): gsa = fp32(max|x|) / 2688 (commit 04cf8ca8,
+// dsv4/layers/router.py, runtime-gsa paragraph). Rows are contiguous and D is
+// a multiple of 16, so the tensor is a flat array of 16-element blocks: block
+// b reads 32 bytes of x at 32 b and writes 8 code bytes at 8 b and one scale
+// byte at b.
+//
+// Two shapes of launch:
+//  * small tensors (<= kSingleBlocks blocks): one workgroup loads every block
+//    into registers, reduces max|x|, derives gsa and quantizes from registers
+//    (x read once, one launch);
+//  * large tensors: amax_partial_kernel writes one max per workgroup, then
+//    quant_kernel folds those partial maxima in every workgroup (a few KB from
+//    L2), derives the same gsa everywhere and quantizes (x read twice: a
+//    tensor-wide max has to be known before the first code is written).
+#include "nvfp4_device.hpp"
+#include "router_internal.hpp"
+
+namespace nvr {
+
+constexpr int kSingleThreads = 512;
+constexpr int kSingleBlocksPerThread = 4;
+
+__device__ __forceinline__ float gsa_from_absmax_bits(uint32_t m) {
+  return __uint_as_float(m << 16) / kGsaDivisor;  // IEEE fp32 division
+}
+
+__device__ __forceinline__ void load_block(const u32x4_t* __restrict__ x, int64_t b, uint32_t* w) {
+  const u32x4_t v0 = __builtin_nontemporal_load(x + 2 * b);
+  const u32x4_t v1 = __builtin_nontemporal_load(x + 2 * b + 1);
+  w[0] = v0[0]; w[1] = v0[1]; w[2] = v0[2]; w[3] = v0[3];
+  w[4] = v1[0]; w[5] = v1[1]; w[6] = v1[2]; w[7] = v1[3];
+}
+
+__device__ __forceinline__ uint32_t vec_absmax(u32x4_t v) {
+  return max(max(bf16_pair_absmax(v[0]), bf16_pair_absmax(v[1])), max(bf16_pair_absmax(v[2]), bf16_pair_absmax(v[3])));
+}
+
+__device__ __forceinline__ uint32_t block_absmax(const uint32_t* w) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, bf16_pair_absmax(w[i]));
+  return m;
+}
+
+// Workgroup-wide max of a per-thread value (blockDim.x threads, multiple of 64).
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+  v = wave_max_u32(v);
+  const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t m = 0;
+  for (int i = 0; i < nwaves; ++i) m = max(m, red[i]);
+  return m;
+}
+
+__global__ __launch_bounds__(kSingleThreads) void quant_single_kernel(const u32x4_t* __restrict__ x, int64_t nblocks,
+                                                                      const float* __restrict__ gsa_override,
+                                                                      uint2* __restrict__ codes,
+                                                                      uint8_t* __restrict__ scales,
+                                                                      float* __restrict__ gsa_out) {
+  __shared__ uint32_t red[kSingleThreads / 64];
+  uint32_t w[kSingleBlocksPerThread][8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < kSingleBlocksPerThread; ++j) {
+    const int64_t b = threadIdx.x + (int64_t)j * kSingleThreads;
+    if (b < nblocks) {
+      load_block(x, b, w[j]);
+      m = max(m, block_absmax(w[j]));
+    }
+  }
+  float gsa;
+  if (gsa_override) {
+    gsa = *gsa_override;
+  } else {
+    gsa = gsa_from_absmax_bits(block_max_u32(m, red));
+  }
+  if (threadIdx.x == 0) *gsa_out = gsa;
+#pragma unroll
+  for (int j = 0; j < kSingleBlocksPerThread; ++j) {
+    const int64_t b = threadIdx.x + (int64_t)j * kSingleThreads;
+    if (b < nblocks) {
+      uint32_t c0, c1, s;
+      quant_block16(w[j], gsa, c0, c1, s);
+      codes[b] = make_uint2(c0, c1);
+      scales[b] = (uint8_t)s;
+    }
+  }
+}
+
+constexpr int kAmaxThreads = 256;
+constexpr int kAmaxUnroll = 4;
+
+__global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const u32x4_t* __restrict__ x, int64_t nvec,
+                                                                    uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[kAmaxThreads / 64];
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+  int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+  for (; i + (kAmaxUnroll - 1) * stride < nvec; i += kAmaxUnroll * stride) {
+    u32x4_t v[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = __builtin_nontemporal_load(x + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) m = max(m, vec_absmax(v[u]));
+  }
+  for (; i < nvec; i += stride) {
+    m = max(m, vec_absmax(__builtin_nontemporal_load(x + i)));
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+constexpr int kQuantThreads = 256;
+
+__global__ __launch_bounds__(kQuantThreads) void quant_kernel(const u32x4_t* __restrict__ x, int64_t nblocks,
+                                                              const uint32_t* __restrict__ partial, int npartial,
+                                                              const float* __restrict__ gsa_override,
+                                                              uint2* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales,
+                                                              float* __restrict__ gsa_out) {
+  __shared__ uint32_t red[kQuantThreads / 64];
+  float gsa;
+  if (gsa_override) {
+    gsa = *gsa_override;
+  } else {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < npartial; i += kQuantThreads) m = max(m, partial[i]);
+    gsa = gsa_from_absmax_bits(block_max_u32(m, red));
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gsa_out = gsa;
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+  for (int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; b < nblocks; b += stride) {
+    uint32_t w[8];
+    load_block(x, b, w);
+    uint32_t c0, c1, s;
+    quant_block16(w, gsa, c0, c1, s);
+    codes[b] = make_uint2(c0, c1);
+    scales[b] = (uint8_t)s;
+  }
+}
+
+__global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t nwords) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+size_t quantize_scratch_bytes() { return (size_t)kAmaxPartials * sizeof(uint32_t); }
+
+hipError_t launch_quantize(const void* x, int64_t rows, int64_t D, const float* gsa_override, uint8_t* codes,
+                           uint8_t* scales, float* gsa_out, void* scratch, hipStream_t stream) {
+  const int64_t nblocks = rows * (D / 16);
+  const u32x4_t* xv = static_cast<const u32x4_t*>(x);
+  uint2* cv = reinterpret_cast<uint2*>(codes);
+  static_assert(kSingleThreads * kSingleBlocksPerThread == kSingleWgMaxBlocks, "single-WG capacity");
+  if (nblocks <= kSingleWgMaxBlocks) {
+    quant_single_kernel<<<1, kSingleThreads, 0, stream>>>(xv, nblocks, gsa_override, cv, scales, gsa_out);
+    return hipGetLastError();
+  }
+  uint32_t* partial = static_cast<uint32_t*>(scratch);
+  int npartial = 0;
+  if (!gsa_override) {
+    const int64_t nvec = nblocks * 2;
+    const int64_t want = (nvec + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
+    npartial = (int)(want < kAmaxPartials ? (want < 1 ? 1 : want) : kAmaxPartials);
+    amax_partial_kernel<<<npartial, kAmaxThreads, 0, stream>>>(xv, nvec, partial);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const int64_t want = (nblocks + kQuantThreads - 1) / kQuantThreads;
+  const int grid = (int)(want < kQuantMaxGrid ? want : kQuantMaxGrid);
+  quant_kernel<<<grid, kQuantThreads, 0, stream>>>(xv, nblocks, partial, npartial, gsa_override, cv, scales,
+                                                   gsa_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
+  const int64_t nwords = (int64_t)(bytes / 4);
+  if (nwords == 0) return hipSuccess;
+  const int64_t want = (nwords + 255) / 256;
+  fill_zero_kernel<<<(int)(want < 1024 ? want : 1024), 256, 0, stream>>>(static_cast<uint32_t*>(p), nwords);
+  return hipGetLastError();
+}
+
+}  // namespace nvr

@@ -1,0 +1,157 @@
+"""Thin ctypes binding of libnvfp4_router.so (argument marshalling only).
+
+Every step of the path runs in the library's HIP kernels; this module only
+checks tensor properties, passes device pointers and the current HIP stream,
+and raises on a non-zero status. PyTorch provides the device memory and the
+stream. There is no fallback: if the library is missing, every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4_router.so")
+
+ROUTER_OK = 0
+EXPORTS = ("router_workspace_bytes", "router_workspace_init", "router_quantize", "router_gate_topk",
+           "router_status_string")
+
+_lib = None
+
+
+class RouterError(RuntimeError):
+    pass
+
+
+def load_library(path=LIB_PATH):
+    """Load the shared library once and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RouterError(f"{path} is not built: run __graft_entry__.build() (hipcc, gfx950)")
+    L = ctypes.CDLL(path)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    L.router_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.router_workspace_bytes.restype = sz
+    L.router_workspace_init.argtypes = [vp, sz, vp]
+    L.router_workspace_init.restype = ctypes.c_int
+    L.router_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+    L.router_quantize.restype = ctypes.c_int
+    L.router_gate_topk.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, i64, i64, i64, i64, vp, vp, vp,
+                                   vp, sz, vp]
+    L.router_gate_topk.restype = ctypes.c_int
+    L.router_status_string.argtypes = [ctypes.c_int]
+    L.router_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != ROUTER_OK:
+        msg = load_library().router_status_string(status).decode()
+        raise RouterError(f"status {status}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _device_tensor(t, name, dtypes, ndim=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise RouterError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise RouterError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise RouterError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise RouterError(f"{name} must have {ndim} dimensions")
+    return t
+
+
+def workspace_bytes(T, D, E, k):
+    n = load_library().router_workspace_bytes(T, D, E, k)
+    if n == 0:
+        raise RouterError(f"invalid sizes T={T} D={D} E={E} k={k}")
+    return int(n)
+
+
+class Workspace:
+    """Caller-owned scratch memory; zero-filled once (its counters must start at zero)."""
+
+    def __init__(self, nbytes, device="cuda"):
+        nbytes = (int(nbytes) + 255) // 256 * 256
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _check(load_library().router_workspace_init(_ptr(self.buf), nbytes, _stream()))
+
+    @classmethod
+    def for_shapes(cls, shapes, device="cuda"):
+        """A workspace large enough for every (T, D, E, k) in ``shapes``."""
+        return cls(max(workspace_bytes(*s) for s in shapes), device)
+
+    @property
+    def nbytes(self):
+        return self.buf.numel()
+
+
+class NVFP4Tensor:
+    """Codes [rows, D/2] uint8, scales [rows, D/16] uint8 and the global scale [1] fp32 on the GPU."""
+
+    def __init__(self, codes, scales, gscale):
+        self.codes, self.scales, self.gscale = codes, scales, gscale
+
+    @property
+    def rows(self):
+        return self.codes.shape[0]
+
+    @property
+    def D(self):
+        return self.codes.shape[1] * 2
+
+
+def empty_nvfp4(rows, D, device="cuda"):
+    return NVFP4Tensor(torch.empty((rows, D // 2), dtype=torch.uint8, device=device),
+                       torch.empty((rows, D // 16), dtype=torch.uint8, device=device),
+                       torch.empty(1, dtype=torch.float32, device=device))
+
+
+def quantize(x, workspace, gsa_override=None, out=None):
+    """router_quantize: bf16 x [rows, D] (bfloat16, or int16/uint16 bit patterns) -> NVFP4Tensor."""
+    _device_tensor(x, "x", (torch.bfloat16, torch.int16, torch.uint16), ndim=2)
+    rows, D = x.shape
+    if out is None:
+        out = empty_nvfp4(rows, D, x.device)
+    if gsa_override is not None:
+        _device_tensor(gsa_override, "gsa_override", (torch.float32,))
+    _check(load_library().router_quantize(_ptr(x), rows, D, _ptr(gsa_override), _ptr(out.codes),
+                                          _ptr(out.scales), _ptr(out.gscale), _ptr(workspace.buf),
+                                          workspace.nbytes, _stream()))
+    return out
+
+
+def gate_topk(xq, wq, bias, k, routed_scale, workspace, want_logits=False, out=None):
+    """router_gate_topk: returns (topk_idx [T,k] int32, topk_w [T,k] fp32, logits [T,E] fp32 or None)."""
+    T, D = xq.rows, xq.D
+    E = wq.rows
+    _device_tensor(bias, "bias", (torch.float32,), ndim=1)
+    for name, t in (("x codes", xq.codes), ("x scales", xq.scales), ("w codes", wq.codes),
+                    ("w scales", wq.scales)):
+        _device_tensor(t, name, (torch.uint8,), ndim=2)
+    if wq.D != D or bias.numel() != E:
+        raise RouterError("gate weights / bias do not match x")
+    if out is None:
+        dev = xq.codes.device
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None)
+    idx, w, logits = out
+    _check(load_library().router_gate_topk(_ptr(xq.codes), _ptr(xq.scales), _ptr(xq.gscale), _ptr(wq.codes),
+                                           _ptr(wq.scales), _ptr(wq.gscale), _ptr(bias), float(routed_scale), T, D,
+                                           E, k, _ptr(idx), _ptr(w), _ptr(logits), _ptr(workspace.buf),
+                                           workspace.nbytes, _stream()))
+    return idx, w, logits

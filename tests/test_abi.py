@@ -1,0 +1,89 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, and its
+host-side logic (status strings, workspace sizing, argument validation) behaves.
+No call here reaches a kernel launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from nvfp4_block_scaled_06_amd import router as rt
+
+HEADER = os.path.join(ROOT, "include", "nvfp4_router.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rt.LIB_PATH):
+        from nvfp4_block_scaled_06_amd import build
+
+        build.build()
+    return rt.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(rt.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.router_status_string(0) == b"ok"
+    for s in (-1, -2, -3):
+        assert lib.router_status_string(s) not in (b"ok", b"unknown status")
+    assert lib.router_status_string(7) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    n = lib.router_workspace_bytes(1, 7168, 256, 8)
+    assert n >= 256 + 4096 and n % 4 == 0
+    assert lib.router_workspace_bytes(64, 7168, 256, 8) >= lib.router_workspace_bytes(1, 7168, 256, 8)
+    assert lib.router_workspace_bytes(8192, 7168, 256, 8) == 256 + 4096  # fused gate needs no scratch
+    for bad in [(1, 7168, 256, 0), (1, 7168, 256, 257), (1, 7169, 256, 8), (-1, 7168, 256, 8), (1, 7168, 0, 1),
+                (1, 7168, 513, 8)]:
+        assert lib.router_workspace_bytes(*bad) == 0, bad
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
+
+
+def test_quantize_rejects_bad_arguments(lib):
+    q = lib.router_quantize
+    assert q(FAKE, 4, 24, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1  # D % 16
+    assert q(FAKE, 4, 0, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert q(FAKE, -1, 256, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert q(None, 4, 256, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert q(ctypes.c_void_p((1 << 20) + 8), 4, 256, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    # Two-pass sizes need workspace scratch.
+    assert q(FAKE, 4096, 7168, None, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert q(FAKE, 4096, 7168, None, FAKE, FAKE, FAKE, FAKE, 256, None) == -1
+
+
+def test_gate_rejects_bad_arguments(lib):
+    g = lib.router_gate_topk
+    args = dict(xc=FAKE, xs=FAKE, gsa=FAKE, wc=FAKE, ws=FAKE, gsw=FAKE, bias=FAKE, r=2.5, T=1, D=7168, E=256, k=8,
+                idx=FAKE, w=FAKE, logits=None, work=FAKE, nbytes=1 << 20, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return g(*a.values())
+
+    assert call(D=7184) == -1  # D % 32
+    assert call(k=0) == -1 and call(k=257) == -1
+    assert call(E=600, k=8) == -2
+    assert call(k=33, E=256) == -2
+    assert call(bias=None) == -1
+    assert call(xc=ctypes.c_void_p((1 << 20) + 4)) == -1
+    assert call(work=None, nbytes=0) == -1  # split gate needs its counters
+    assert call(nbytes=100) == -1
