@@ -48,6 +48,12 @@ def quant_bytes(c):
     return reads * 2 * c.T * c.D + c.T * c.D * 9 // 16 + 4
 
 
+def forward_bytes(c):
+    """Algorithmic bytes of one single-launch router call: W, x (bf16) and bias read; codes, scales, gsa and
+    routing written."""
+    return c.E * c.D * 9 // 16 + 2 * c.T * c.D + 4 * c.E + c.T * c.D * 9 // 16 + 4 + 8 * c.T * c.k
+
+
 def gate_flops(c):
     return 2 * c.T * c.E * c.D
 
@@ -94,7 +100,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=2, help="router shape 1..5 (2 = decode T=1)")
-    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -129,25 +135,24 @@ def main():
     torch.cuda.synchronize()
     log("inputs resident")
 
-    def step(i):
+    def step_forward(i):
+        l = i % c.layers
+        rt.forward(xs[l], wq[l], bias[l], c.k, c.routed_scale, ws, xq=xq, out=out)
+
+    def step_two_calls(i):
         l = i % c.layers
         rt.quantize(xs[l], ws, out=xq)
         rt.gate_topk(xq, wq[l], bias[l], c.k, c.routed_scale, ws, out=out)
 
-    for i in range(W):
-        step(i)
-    torch.cuda.synchronize()
+    def time_eager(step):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(W + i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
 
-    # Eager rate.
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(W + i)
-    torch.cuda.synchronize()
-    eager_s = time.perf_counter() - t0
-    log(f"eager: {eager_s / K * 1e6:.2f} us/call")
-
-    graph_s = None
-    if not args.eager:
+    def time_graph(step):
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -161,36 +166,57 @@ def main():
         t0 = time.perf_counter()
         g.replay()
         torch.cuda.synchronize()
-        graph_s = time.perf_counter() - t0
-        log(f"graph: {graph_s / K * 1e6:.2f} us/call")
-    timed_s = eager_s if graph_s is None else graph_s
+        dt = time.perf_counter() - t0
+        del g
+        return dt
 
-    # Per-kernel durations with events on the launch stream (eager launches).
+    for step in (step_forward, step_two_calls):
+        for i in range(W):
+            step(i)
+    torch.cuda.synchronize()
+
+    eager_fwd = time_eager(step_forward)
+    eager_two = time_eager(step_two_calls)
+    log(f"eager: forward {eager_fwd / K * 1e6:.2f} us/call, quantize+gate {eager_two / K * 1e6:.2f} us/call")
+    graph_fwd = graph_two = None
+    if not args.eager:
+        graph_two = time_graph(step_two_calls)
+        graph_fwd = time_graph(step_forward)
+        log(f"graph: forward {graph_fwd / K * 1e6:.2f} us/call, quantize+gate {graph_two / K * 1e6:.2f} us/call")
+    timed_s = eager_fwd if graph_fwd is None else graph_fwd
+
+    # Per-launch durations from HIP events on the launch stream (eager launches).
     nk = min(K, 500)
     cur = torch.cuda.current_stream()
-    evq = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
-    evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
-    for i in range(nk):
-        l = (W + i) % c.layers
-        evq[i][0].record(cur)
-        rt.quantize(xs[l], ws, out=xq)
-        evq[i][1].record(cur)
-        evg[i][0].record(cur)
-        rt.gate_topk(xq, wq[l], bias[l], c.k, c.routed_scale, ws, out=out)
-        evg[i][1].record(cur)
-    torch.cuda.synchronize()
-    tq = float(np.mean([a.elapsed_time(b) for a, b in evq])) * 1e-3
-    tg = float(np.mean([a.elapsed_time(b) for a, b in evg])) * 1e-3
-    log(f"kernel times: quantize {tq * 1e6:.2f} us, gate {tg * 1e6:.2f} us")
 
-    if c.T >= 4096:
+    def event_time(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
+        for i in range(nk):
+            ev[i][0].record(cur)
+            fn(W + i)
+            ev[i][1].record(cur)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+    tf = event_time(step_forward)
+    tq = event_time(lambda i: rt.quantize(xs[i % c.layers], ws, out=xq))
+    tg = event_time(lambda i: rt.gate_topk(xq, wq[i % c.layers], bias[i % c.layers], c.k, c.routed_scale, ws,
+                                           out=out))
+    log(f"launch times: forward {tf * 1e6:.2f} us, quantize {tq * 1e6:.2f} us, gate {tg * 1e6:.2f} us")
+
+    if c.T > 4:
         achieved = gate_flops(c) / tg / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None, "kernel": "gate (fused MFMA + top-k)"}
+                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                "kernel": "gate_fused_kernel" if c.T > 256 else "gate_tile_kernel",
+                "algorithmic": f"{gate_flops(c)} FLOP per launch"}
     else:
-        achieved = gate_bytes(c) / tg / 1e9
+        nbytes = forward_bytes(c)
+        achieved = nbytes / tf / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gate (split GEMV-MFMA + top-k)"}
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "gate_gemv_kernel (quantizing, single launch per call)",
+                "algorithmic": f"{nbytes} B per launch"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -214,11 +240,14 @@ def main():
         "config": {
             "workload": f"{c.name} router T={c.T} D={c.D} E={c.E} k={c.k}, {c.layers} layer set(s) cycled",
             "T": c.T, "D": c.D, "E": c.E, "k": c.k,
-            "launch": "eager" if graph_s is None else "hipgraph",
+            "entry": "router_forward",
+            "launch": "eager" if graph_fwd is None else "hipgraph",
             "us_per_call": ms * 1e3,
-            "eager_us_per_call": eager_s / K * 1e6,
-            "quantize_kernel_us": tq * 1e6,
-            "gate_kernel_us": tg * 1e6,
+            "eager_us_per_call": eager_fwd / K * 1e6,
+            "two_call_us_per_call": (eager_two if graph_two is None else graph_two) / K * 1e6,
+            "forward_launch_us": tf * 1e6,
+            "quantize_launch_us": tq * 1e6,
+            "gate_launch_us": tg * 1e6,
             "parallelism": "single GPU",
         },
         "roofline": roof,

@@ -26,6 +26,8 @@
  *     so calls may be captured in a HIP graph.
  *   - A negative return value means the arguments were rejected on the host
  *     and nothing was enqueued, except ROUTER_EHIP (a launch failed).
+ *   - Data pointers of an empty batch (rows or T == 0) may be NULL; the
+ *     global scale output is still written (0, or the override).
  *   - Non-finite input values are a precondition violation: they make the
  *     global scale non-finite (the device-visible error flag) and leave the
  *     other outputs unspecified.
@@ -118,6 +120,25 @@ int router_gate_topk(const uint8_t* x_codes, const uint8_t* x_scales, const floa
                      const uint8_t* w_scales, const float* gsw, const float* bias, float routed_scale, int64_t T,
                      int64_t D, int64_t E, int64_t k, int32_t* topk_idx, float* topk_w, float* logits_out,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * router_quantize followed by router_gate_topk, in one call and with the same
+ * results: x_codes, x_scales and gsa_out are written exactly as
+ * router_quantize writes them, and the routing is that of router_gate_topk on
+ * them. For decode-size batches (T <= 4) it is a single kernel launch (the
+ * single-launch fused router that commit 04cf8ca8, dsv4/layers/router.py,
+ * gives priority over the two-launch path): every workgroup derives gsa from
+ * all of x and quantizes the blocks it multiplies in registers. Larger T runs
+ * the quantize kernels and then the gate kernels on the stream.
+ *
+ * Arguments as in the two calls above: x [T, D] bf16 (16-byte aligned);
+ * x_codes (16-byte aligned), x_scales and gsa_out are outputs; D % 32 == 0.
+ * The workspace must satisfy router_workspace_bytes(T, D, E, k).
+ */
+int router_forward(const void* x, int64_t T, int64_t D, const float* gsa_override, uint8_t* x_codes,
+                   uint8_t* x_scales, float* gsa_out, const uint8_t* w_codes, const uint8_t* w_scales,
+                   const float* gsw, const float* bias, float routed_scale, int64_t E, int64_t k, int32_t* topk_idx,
+                   float* topk_w, float* logits_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* router_status_string(int status);

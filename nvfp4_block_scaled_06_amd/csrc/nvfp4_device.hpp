@@ -173,16 +173,77 @@ __device__ __forceinline__ half8_t fp4x8_to_f16(uint32_t c, _Float16 s) {
 
 __device__ __forceinline__ _Float16 e4m3_f16(uint32_t b) { return (_Float16)e4m3_value(b); }
 
+// Eight E2M1 codes as their exact fp16 values, in the hardware conversion's
+// element order (scale operand 1.0: the conversion applies only the exponent
+// of its scale operand, so block scales are multiplied separately).
+__device__ __forceinline__ half8_t fp4x8_q(uint32_t c) {
+  const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0);
+  const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1);
+  const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2);
+  const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3);
+  return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// sum_i a_i * b_i over 8 fp16 pairs with fp32 accumulation. For E2M1 code
+// values every product (|q q| <= 36, a multiple of 1/4) and every partial sum
+// is exact in fp32.
+__device__ __forceinline__ float dot8(half8_t a, half8_t b, float acc) {
+  acc = __builtin_amdgcn_fdot2(half2_t{a[0], a[1]}, half2_t{b[0], b[1]}, acc, false);
+  acc = __builtin_amdgcn_fdot2(half2_t{a[2], a[3]}, half2_t{b[2], b[3]}, acc, false);
+  acc = __builtin_amdgcn_fdot2(half2_t{a[4], a[5]}, half2_t{b[4], b[5]}, acc, false);
+  acc = __builtin_amdgcn_fdot2(half2_t{a[6], a[7]}, half2_t{b[6], b[7]}, acc, false);
+  return acc;
+}
+
+// Wavefront-wide reductions with DPP row operations (VALU latency, no LDS
+// crossbar): xor-1 and xor-2 quad permutes, the 8-lane and 16-lane mirrors
+// leave every lane with its 16-lane row's result; four readlanes finish.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7-i within 8
+constexpr int kDppMirror = 0x140;      // lane i <- 15-i within 16
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  v = fmaxf(v, __int_as_float(dpp_i<kDppXor1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_i<kDppXor2>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_i<kDppMirror>(__float_as_int(v))));
+  const int iv = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(iv, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(iv, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(iv, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(iv, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-  return v;
+  v = max(v, (uint32_t)dpp_i<kDppXor1>((int)v));
+  v = max(v, (uint32_t)dpp_i<kDppXor2>((int)v));
+  v = max(v, (uint32_t)dpp_i<kDppHalfMirror>((int)v));
+  v = max(v, (uint32_t)dpp_i<kDppMirror>((int)v));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Sum over the wavefront in a fixed order (deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(dpp_i<kDppXor1>(__float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppXor2>(__float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppMirror>(__float_as_int(v)));
+  const int iv = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(iv, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(iv, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(iv, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(iv, 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // Six-step routing of one token by one wavefront (commit e0f60b9f,
@@ -241,7 +302,7 @@ __device__ __forceinline__ void wave_route_row(const float* Lrow, const float* _
 #pragma unroll
     for (int j = 0; j < JMAX; ++j)
       if (j == wj) sv = s[j];
-    sv = __shfl(sv, wl, 64);
+    sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), wl));
     if (lane == wl) live &= ~(1u << wj);
     if (lane == r) {
       my_idx = win;

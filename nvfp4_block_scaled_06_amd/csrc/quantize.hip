@@ -29,8 +29,8 @@ __device__ __forceinline__ float gsa_from_absmax_bits(uint32_t m) {
 }
 
 __device__ __forceinline__ void load_block(const u32x4_t* __restrict__ x, int64_t b, uint32_t* w) {
-  const u32x4_t v0 = __builtin_nontemporal_load(x + 2 * b);
-  const u32x4_t v1 = __builtin_nontemporal_load(x + 2 * b + 1);
+  const u32x4_t v0 = x[2 * b];
+  const u32x4_t v1 = x[2 * b + 1];
   w[0] = v0[0]; w[1] = v0[1]; w[2] = v0[2]; w[3] = v0[3];
   w[4] = v1[0]; w[5] = v1[1]; w[6] = v1[2]; w[7] = v1[3];
 }

@@ -21,6 +21,11 @@ bool shape_ok(int64_t rows, int64_t D) {
 
 int status_from(hipError_t e) { return e == hipSuccess ? ROUTER_OK : ROUTER_EHIP; }
 
+size_t gate_need(int64_t T, int64_t D, int64_t E) {
+  if (T == 0 || nvr::gate_kind(T, D) == nvr::GateKind::kFused) return 0;
+  return nvr::kCounterBytes + nvr::gate_scratch_bytes(T, D, E);
+}
+
 size_t quantize_need(int64_t rows, int64_t D, bool override_given) {
   const int64_t nblocks = rows * (D / 16);
   // The single-workgroup path needs no scratch; the two-pass path keeps one
@@ -50,7 +55,7 @@ int router_workspace_init(void* workspace, size_t bytes, void* stream) {
 int router_quantize(const void* x, int64_t rows, int64_t D, const float* gsa_override, uint8_t* codes,
                     uint8_t* scales, float* gsa_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!shape_ok(rows, D)) return ROUTER_EINVAL;
-  if (!x || !codes || !scales || !gsa_out) return ROUTER_EINVAL;
+  if (!gsa_out || (rows > 0 && (!x || !codes || !scales))) return ROUTER_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(gsa_out, 4)) return ROUTER_EINVAL;
   if (gsa_override && !aligned(gsa_override, 4)) return ROUTER_EINVAL;
   const size_t need = quantize_need(rows, D, gsa_override != nullptr);
@@ -60,27 +65,72 @@ int router_quantize(const void* x, int64_t rows, int64_t D, const float* gsa_ove
                                           static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+int check_gate_args(const uint8_t* x_codes, const uint8_t* x_scales, const float* gsa, const uint8_t* w_codes,
+                    const uint8_t* w_scales, const float* gsw, const float* bias, int64_t T, int64_t D, int64_t E,
+                    int64_t k, const int32_t* topk_idx, const float* topk_w, const float* logits_out,
+                    const void* workspace, size_t workspace_bytes) {
+  if (!shape_ok(T, D) || D % 32 != 0) return ROUTER_EINVAL;
+  if (E < 1 || k < 1 || k > E) return ROUTER_EINVAL;
+  if (E > ROUTER_MAX_EXPERTS || k > ROUTER_MAX_TOPK) return ROUTER_EUNSUPPORTED;
+  if (!gsa || !w_codes || !w_scales || !gsw || !bias) return ROUTER_EINVAL;
+  if (T > 0 && (!x_codes || !x_scales || !topk_idx || !topk_w)) return ROUTER_EINVAL;
+  if (!aligned(x_codes, 16) || !aligned(w_codes, 16) || !aligned(x_scales, 2) || !aligned(w_scales, 2) ||
+      !aligned(gsa, 4) || !aligned(gsw, 4) || !aligned(bias, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
+      !aligned(logits_out, 4))
+    return ROUTER_EINVAL;
+  const size_t need = gate_need(T, D, E);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return ROUTER_EINVAL;
+  return ROUTER_OK;
+}
+
+}  // namespace
+
 int router_gate_topk(const uint8_t* x_codes, const uint8_t* x_scales, const float* gsa, const uint8_t* w_codes,
                      const uint8_t* w_scales, const float* gsw, const float* bias, float routed_scale, int64_t T,
                      int64_t D, int64_t E, int64_t k, int32_t* topk_idx, float* topk_w, float* logits_out,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (!shape_ok(T, D) || D % 32 != 0) return ROUTER_EINVAL;
-  if (E < 1 || k < 1 || k > E) return ROUTER_EINVAL;
-  if (E > ROUTER_MAX_EXPERTS || k > ROUTER_MAX_TOPK) return ROUTER_EUNSUPPORTED;
-  if (!x_codes || !x_scales || !gsa || !w_codes || !w_scales || !gsw || !bias || !topk_idx || !topk_w)
-    return ROUTER_EINVAL;
-  if (!aligned(x_codes, 16) || !aligned(w_codes, 16) || !aligned(x_scales, 2) || !aligned(w_scales, 2) ||
-      !aligned(gsa, 4) || !aligned(gsw, 4) || !aligned(bias, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
-      (logits_out && !aligned(logits_out, 4)))
-    return ROUTER_EINVAL;
-  size_t need = 0;
-  if (T > 0 && nvr::use_split_gate(T)) need = nvr::kCounterBytes + nvr::gate_scratch_bytes(T, D, E);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return ROUTER_EINVAL;
-  uint32_t* counters = need > 0 ? static_cast<uint32_t*>(workspace) : nullptr;
-  void* scratch = need > 0 ? static_cast<char*>(workspace) + nvr::kCounterBytes : nullptr;
+  const int st = check_gate_args(x_codes, x_scales, gsa, w_codes, w_scales, gsw, bias, T, D, E, k, topk_idx, topk_w,
+                                 logits_out, workspace, workspace_bytes);
+  if (st != ROUTER_OK) return st;
+  const bool ws = gate_need(T, D, E) > 0;
+  uint32_t* counters = ws ? static_cast<uint32_t*>(workspace) : nullptr;
+  void* scratch = ws ? static_cast<char*>(workspace) + nvr::kCounterBytes : nullptr;
   return status_from(nvr::launch_gate(x_codes, x_scales, gsa, w_codes, w_scales, gsw, bias, routed_scale, T, D, E,
                                       k, topk_idx, topk_w, logits_out, counters, scratch,
                                       static_cast<hipStream_t>(stream)));
+}
+
+int router_forward(const void* x, int64_t T, int64_t D, const float* gsa_override, uint8_t* x_codes,
+                   uint8_t* x_scales, float* gsa_out, const uint8_t* w_codes, const uint8_t* w_scales,
+                   const float* gsw, const float* bias, float routed_scale, int64_t E, int64_t k, int32_t* topk_idx,
+                   float* topk_w, float* logits_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!shape_ok(T, D)) return ROUTER_EINVAL;
+  if (!gsa_out || (T > 0 && !x) || !aligned(x, 16) || !aligned(gsa_out, 4) ||
+      (gsa_override && !aligned(gsa_override, 4)))
+    return ROUTER_EINVAL;
+  int st = check_gate_args(x_codes, x_scales, gsa_out, w_codes, w_scales, gsw, bias, T, D, E, k, topk_idx, topk_w,
+                           logits_out, workspace, workspace_bytes);
+  if (st != ROUTER_OK) return st;
+  const size_t qneed = quantize_need(T, D, gsa_override != nullptr);
+  if (qneed > 0 && (!workspace || workspace_bytes < qneed || !aligned(workspace, 256))) return ROUTER_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  if (T > 0 && nvr::forward_single_launch(T, D)) {
+    return status_from(nvr::launch_forward_fused(x, gsa_override, x_codes, x_scales, gsa_out, w_codes, w_scales, gsw,
+                                                 bias, routed_scale, T, D, E, k, topk_idx, topk_w, logits_out,
+                                                 reinterpret_cast<uint32_t*>(base), base + nvr::kCounterBytes, s));
+  }
+  // Larger T: the quantize kernels then the gate kernels, back to back on the stream.
+  hipError_t err = nvr::launch_quantize(x, T, D, gsa_override, x_codes, x_scales, gsa_out,
+                                        qneed > 0 ? base + nvr::kCounterBytes : nullptr, s);
+  if (err != hipSuccess) return ROUTER_EHIP;
+  const bool ws = gate_need(T, D, E) > 0;
+  return status_from(nvr::launch_gate(x_codes, x_scales, gsa_out, w_codes, w_scales, gsw, bias, routed_scale, T, D,
+                                      E, k, topk_idx, topk_w, logits_out,
+                                      ws ? reinterpret_cast<uint32_t*>(base) : nullptr,
+                                      ws ? base + nvr::kCounterBytes : nullptr, s));
 }
 
 const char* router_status_string(int status) {

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4_router.so")
 
 ROUTER_OK = 0
 EXPORTS = ("router_workspace_bytes", "router_workspace_init", "router_quantize", "router_gate_topk",
-           "router_status_string")
+           "router_forward", "router_status_string")
 
 _lib = None
 
@@ -43,6 +43,9 @@ def load_library(path=LIB_PATH):
     L.router_gate_topk.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, i64, i64, i64, i64, vp, vp, vp,
                                    vp, sz, vp]
     L.router_gate_topk.restype = ctypes.c_int
+    L.router_forward.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, i64, i64, vp, vp,
+                                 vp, vp, sz, vp]
+    L.router_forward.restype = ctypes.c_int
     L.router_status_string.argtypes = [ctypes.c_int]
     L.router_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -56,7 +59,7 @@ def _check(status):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None or t.numel() == 0 else ctypes.c_void_p(t.data_ptr())
 
 
 def _stream():
@@ -155,3 +158,30 @@ def gate_topk(xq, wq, bias, k, routed_scale, workspace, want_logits=False, out=N
                                            E, k, _ptr(idx), _ptr(w), _ptr(logits), _ptr(workspace.buf),
                                            workspace.nbytes, _stream()))
     return idx, w, logits
+
+
+def forward(x, wq, bias, k, routed_scale, workspace, gsa_override=None, want_logits=False, xq=None, out=None):
+    """router_forward: quantize x and route it in one call.
+
+    Returns ``(xq, (topk_idx, topk_w, logits or None))``; ``xq`` holds x's NVFP4 codes, scales and gsa.
+    """
+    _device_tensor(x, "x", (torch.bfloat16, torch.int16, torch.uint16), ndim=2)
+    T, D = x.shape
+    E = wq.rows
+    _device_tensor(bias, "bias", (torch.float32,), ndim=1)
+    if wq.D != D or bias.numel() != E:
+        raise RouterError("gate weights / bias do not match x")
+    if gsa_override is not None:
+        _device_tensor(gsa_override, "gsa_override", (torch.float32,))
+    if xq is None:
+        xq = empty_nvfp4(T, D, x.device)
+    if out is None:
+        dev = x.device
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None)
+    idx, w, logits = out
+    _check(load_library().router_forward(_ptr(x), T, D, _ptr(gsa_override), _ptr(xq.codes), _ptr(xq.scales),
+                                         _ptr(xq.gscale), _ptr(wq.codes), _ptr(wq.scales), _ptr(wq.gscale),
+                                         _ptr(bias), float(routed_scale), E, k, _ptr(idx), _ptr(w), _ptr(logits),
+                                         _ptr(workspace.buf), workspace.nbytes, _stream()))
+    return xq, out

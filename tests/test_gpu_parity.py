@@ -330,3 +330,75 @@ def test_graph_capture_replays_match_eager(dev, ws, cfg):
         torch.cuda.synchronize()
         for a, b in zip(out, eager):
             assert torch.equal(a, b), f"replay {rep} differs"
+
+
+# ----------------------------------------------------------------------------- router_forward
+
+
+@pytest.mark.parametrize("cfg,T,D,E,k", [(2, 1, 7168, 256, 8), (None, 3, 7168, 256, 8), (None, 4, 2048, 384, 8),
+                                         (None, 2, 16384, 64, 4), (None, 9, 7168, 256, 8), (1, 4, 256, 16, 2)])
+def test_forward_matches_oracle(dev, ws, cfg, T, D, E, k):
+    """router_forward (single launch at decode sizes) gives the quantizer's bytes and the oracle's routing."""
+    if cfg is not None:
+        x, w, bias = wl.make_x(cfg), wl.make_w(cfg), wl.make_bias(cfg)
+        r = wl.CONFIGS[cfg].routed_scale
+    else:
+        x, w = synth((T, D), 7 * T + D), synth((E, D), 11 * E + D, 0.02)
+        bias = np.random.default_rng(E + T).uniform(-0.01, 0.01, E).astype(np.float32)
+        r = 2.5
+    log(f"forward T={T} D={D} E={E} k={k}")
+    wq = gpu_quant(w, dev, ws)
+    b = torch.from_numpy(bias).to(dev)
+    xq, (idx, wts, logits) = rt.forward(to_dev(x, dev), wq, b, k, r, ws, want_logits=True)
+    torch.cuda.synchronize()
+    ref = router_ref.router_ref(x, w, bias, k, r)
+    assert_quant(xq, ref["xq"], "x via router_forward")
+    assert_route(ref, idx.cpu().numpy(), wts.cpu().numpy(), logits.cpu().numpy(), k, r, f"forward T={T}")
+
+
+def test_forward_static_scale_override(dev, ws):
+    c = wl.CONFIGS[2]
+    x, w, bias = wl.make_x(2, 3), wl.make_w(2, 3), wl.make_bias(2, 3)
+    ov = float(quant_ref.gsa_ref(quant_ref.amax_ref(x))) / 4
+    log("forward with gsa override")
+    wq = gpu_quant(w, dev, ws)
+    xq, (idx, wts, logits) = rt.forward(to_dev(x, dev), wq, torch.from_numpy(bias).to(dev), c.k, c.routed_scale, ws,
+                                        gsa_override=torch.tensor([ov], dtype=torch.float32, device=dev),
+                                        want_logits=True)
+    torch.cuda.synchronize()
+    ref = router_ref.router_ref(x, w, bias, c.k, c.routed_scale, gsa_override=ov)
+    assert_quant(xq, ref["xq"], "x (override)")
+    assert_route(ref, idx.cpu().numpy(), wts.cpu().numpy(), logits.cpu().numpy(), c.k, c.routed_scale, "override")
+
+
+def test_forward_graph_replay_cycles_layers(dev, ws):
+    """Decode loop as the benchmark runs it: several layer sets captured in one graph, replayed twice."""
+    c = wl.CONFIGS[2]
+    L = 5
+    xs = [to_dev(wl.make_x(2, l), dev) for l in range(L)]
+    wqs = [gpu_quant(wl.make_w(2, l), dev, ws) for l in range(L)]
+    bs = [torch.from_numpy(wl.make_bias(2, l)).to(dev) for l in range(L)]
+    xq = [rt.empty_nvfp4(1, c.D, dev) for _ in range(L)]
+    outs = [(torch.empty((1, c.k), dtype=torch.int32, device=dev), torch.empty((1, c.k), dtype=torch.float32, device=dev),
+             None) for _ in range(L)]
+    log("forward graph replay")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for l in range(L):
+                rt.forward(xs[l], wqs[l], bs[l], c.k, c.routed_scale, ws, xq=xq[l], out=outs[l])
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(2):
+        for o in outs:
+            o[0].zero_()
+            o[1].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            ref = router_ref.router_ref(wl.make_x(2, l), wl.make_w(2, l), wl.make_bias(2, l), c.k, c.routed_scale)
+            fails = check.check_topk(outs[l][0].cpu().numpy(), outs[l][1].cpu().numpy(), ref["s"], ref["b"], c.k,
+                                     c.routed_scale)
+            assert not fails, f"replay {rep} layer {l}: " + "; ".join(fails)
