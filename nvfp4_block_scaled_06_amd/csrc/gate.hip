@@ -8,11 +8,11 @@
 // L2, so they never make an HBM round trip unless logits_out asks for them.
 //
 // Three kernels, by token count T:
-//  * gemv (T <= 4, decode): one workgroup per 4 experts, K split over its
-//    threads (one 16-element block each), dot products of exact fp16 code
-//    values on the VALU, a fixed-order workgroup sum; the last workgroup to
-//    arrive (device arrival counter) routes every token. A variant also
-//    quantizes x itself (router_forward: one launch per router call).
+//  * decode (T <= 4): one workgroup per 128-element K slice; dot products of
+//    exact fp16 code values on the VALU, slice partials through the
+//    workspace, and the last workgroup to arrive (device arrival counter)
+//    adds them and routes every token. A variant also quantizes x itself
+//    (router_forward: one launch per router call).
 //  * tile (T <= 256): 16x16 output tiles on 16x16x32 f16 MFMAs, the four
 //    waves of a workgroup splitting K and summing through LDS; the last
 //    workgroup of each 16-row tile routes it.
@@ -93,12 +93,18 @@ __device__ __forceinline__ void release_counter(uint32_t* counter) {
 }
 
 // ---------------------------------------------------------------------------
-// gemv: decode-size T.
+// decode: T <= 4. The K axis is split into slices of 8 blocks (128 elements),
+// one workgroup per slice. Each workgroup reads all of x for the global max
+// (the quantizing variant; a few KB from L2), quantizes only its own slice,
+// and forms the slice's partial dot products for every expert: lane group q
+// owns experts q, q+64, ..., lane r of the group one K block, and an 8-lane
+// segmented sum gives the slice partial. The last workgroup to arrive adds
+// the slice partials in slice order and routes every token.
 // ---------------------------------------------------------------------------
-struct GemvArgs {
+struct DecodeArgs {
   const u32x4_t* x;           // bf16 x [T, D] (quantizing variant only)
   const float* gsa_override;  // quantizing variant only; NULL = runtime gsa
-  uint8_t* xc;                // x codes [T, D/2]: written by workgroup 0 (quantizing) or read
+  uint8_t* xc;                // x codes [T, D/2]: written slice by slice (quantizing) or read
   uint8_t* xs;                // x scales [T, D/16]: likewise
   float* gsa;                 // [1]: written by workgroup 0 (quantizing) or read
   const uint8_t* wc;
@@ -110,166 +116,186 @@ struct GemvArgs {
   int32_t* idx;
   float* w;
   float* logits_out;
-  float* lbuf;  // [T, E] workspace
+  unsigned long long* acc;  // [T, E] fixed-point logit accumulators (zero between calls)
   uint32_t* counter;
 };
 
-constexpr int kGemvMaxT = 4;
-constexpr int kGemvMaxThreads = 512;
-constexpr int kGemvExperts = 4;  // experts per workgroup: E/4 arrivals on the counter
+constexpr int kDecMaxT = 4;
+constexpr int kDecThreads = 512;
+constexpr int kDecSliceBlocks = 8;   // K blocks per slice (one per lane of an 8-lane group)
+constexpr int kDecAmaxChunks = 8;    // 16-byte chunks of x per thread in the first max pass
 
-template <int TMAX, int BPT, int JMAX, bool QUANT>
-__global__ __launch_bounds__(kGemvMaxThreads) void gate_gemv_kernel(GemvArgs a) {
-  constexpr int EPW = kGemvExperts;
-  __shared__ float red[kGemvMaxThreads / 64][EPW][TMAX];
-  __shared__ uint32_t ured[kGemvMaxThreads / 64];
-  __shared__ float lg[TMAX * 512];
+template <int EP, bool QUANT>
+__global__ __launch_bounds__(kDecThreads) void gate_decode_kernel(DecodeArgs a) {
+  __shared__ uint32_t xq_lds[kDecMaxT][kDecSliceBlocks][2];
+  __shared__ uint32_t xsb_lds[kDecMaxT][kDecSliceBlocks];
+  __shared__ uint32_t ured[kDecThreads / 64];
+  __shared__ float lg[kDecMaxT * 512];
+  __shared__ float bias_s[512];
+  __shared__ WaveRouteScratch<EP> rsc[kDecMaxT];
   __shared__ uint32_t s_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
-  const int e0 = blockIdx.x * EPW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = tid >> 3, r = tid & 7;
+  const int ks = blockIdx.x, nslices = gridDim.x;
   const int nb = a.D >> 4;
-  const int T = a.T;
+  const int kb0 = ks * kDecSliceBlocks;
+  const int nkb = min(kDecSliceBlocks, nb - kb0);
+  const int T = a.T, E = a.E;
+  const int64_t rowc = a.D / 2;
 
-  // Gate-weight blocks of this workgroup's experts (8 code bytes + 1 scale
-  // byte each), issued first so their latency overlaps the activation work.
-  uint32_t wq[EPW][BPT][2], wsb[EPW][BPT];
+  // Bias, for the last workgroup; gate-weight blocks of this lane.
+  const float bias0 = tid < E ? a.bias[tid] : 0.0f;
+  uint32_t wq[EP][2], wsb[EP];
 #pragma unroll
-  for (int p = 0; p < EPW; ++p)
-#pragma unroll
-    for (int b = 0; b < BPT; ++b) {
-      const int j = tid + b * blockDim.x, e = e0 + p;
-      wq[p][b][0] = wq[p][b][1] = 0u;
-      wsb[p][b] = 0u;
-      if (j < nb && e < a.E) {
-        const uint2 v = *reinterpret_cast<const uint2*>(a.wc + (int64_t)e * (a.D / 2) + 8 * j);
-        wq[p][b][0] = v.x;
-        wq[p][b][1] = v.y;
-        wsb[p][b] = a.ws[(int64_t)e * nb + j];
-      }
+  for (int p = 0; p < EP; ++p) {
+    const int e = q + 64 * p;
+    wq[p][0] = wq[p][1] = 0u;
+    wsb[p] = 0u;
+    if (e < E && r < nkb) {
+      const int j = kb0 + r;
+      const uint2 v = *reinterpret_cast<const uint2*>(a.wc + (int64_t)e * rowc + 8 * j);
+      wq[p][0] = v.x;
+      wq[p][1] = v.y;
+      wsb[p] = a.ws[(int64_t)e * nb + j];
     }
+  }
 
-  uint32_t xq[TMAX][BPT][2], xsb[TMAX][BPT];
+  // The slice's x blocks: thread (t, kb) = (tid / 8, tid % 8) for tid < 8 T.
+  const int qt = tid >> 3, qkb = tid & 7;
+  const bool quantizer = tid < T * kDecSliceBlocks && qkb < nkb;
+  const int64_t qblock = (int64_t)qt * nb + kb0 + qkb;
   float gsa;
+  uint32_t c0 = 0u, c1 = 0u, sb = 0u;
   if constexpr (QUANT) {
-    // Every workgroup reads all of x (T*D*2 bytes, from L2 after the first)
-    // and derives the same gsa; each thread quantizes the blocks it owns.
-    uint32_t raw[TMAX][BPT][8];
+    // Every load is issued before the first use: the slice block this lane
+    // quantizes, and the first (usually only) pass of 16-byte chunks of x
+    // for the global max. Predicated by lane, never by a uniform branch.
+    const int n16 = T * nb * 2;
+    u32x4_t v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+    if (quantizer) {
+      v0 = a.x[2 * qblock];
+      v1 = a.x[2 * qblock + 1];
+    }
+    u32x4_t xv[kDecAmaxChunks];
+#pragma unroll
+    for (int c = 0; c < kDecAmaxChunks; ++c) {
+      const int i = tid + c * kDecThreads;
+      xv[c] = i < n16 ? a.x[i] : u32x4_t{0u, 0u, 0u, 0u};
+    }
     uint32_t m = 0;
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t)
-#pragma unroll
-      for (int b = 0; b < BPT; ++b) {
-        const int j = tid + b * blockDim.x;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) raw[t][b][i] = 0u;
-        if (t < T && j < nb) {
-          const u32x4_t v0 = a.x[2 * ((int64_t)t * nb + j)];
-          const u32x4_t v1 = a.x[2 * ((int64_t)t * nb + j) + 1];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            raw[t][b][i] = v0[i];
-            raw[t][b][4 + i] = v1[i];
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i) m = max(m, bf16_pair_absmax(raw[t][b][i]));
-        }
-      }
-    if (a.gsa_override) {
-      gsa = *a.gsa_override;
-    } else {
-      m = wave_max_u32(m);
-      if (lane == 0) ured[wave] = m;
-      __syncthreads();
-      uint32_t mm = 0;
-      for (int i = 0; i < nwaves; ++i) mm = max(mm, ured[i]);
-      gsa = __uint_as_float(mm << 16) / kGsaDivisor;
+    for (int c = 0; c < kDecAmaxChunks; ++c)
+      m = max(m, max(max(bf16_pair_absmax(xv[c][0]), bf16_pair_absmax(xv[c][1])),
+                     max(bf16_pair_absmax(xv[c][2]), bf16_pair_absmax(xv[c][3]))));
+    for (int i = tid + kDecAmaxChunks * kDecThreads; i < n16; i += kDecThreads) {  // very large T * D only
+      const u32x4_t v = a.x[i];
+      m = max(m, max(max(bf16_pair_absmax(v[0]), bf16_pair_absmax(v[1])),
+                     max(bf16_pair_absmax(v[2]), bf16_pair_absmax(v[3]))));
     }
+    m = wave_max_u32(m);
+    if (lane == 0) ured[wave] = m;
+    __syncthreads();
+    uint32_t mm = 0;
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t)
+    for (int i = 0; i < kDecThreads / 64; ++i) mm = max(mm, ured[i]);
+    gsa = a.gsa_override ? *a.gsa_override : __uint_as_float(mm << 16) / kGsaDivisor;
+    if (quantizer) {
+      uint32_t raw[8];
 #pragma unroll
-      for (int b = 0; b < BPT; ++b) {
-        const int j = tid + b * blockDim.x;
-        uint32_t s = 0u;
-        xq[t][b][0] = xq[t][b][1] = 0u;
-        if (t < T) quant_block16(raw[t][b], gsa, xq[t][b][0], xq[t][b][1], s);
-        xsb[t][b] = s;
-        if (blockIdx.x == 0 && t < T && j < nb) {
-          *reinterpret_cast<uint2*>(a.xc + ((int64_t)t * nb + j) * 8) = make_uint2(xq[t][b][0], xq[t][b][1]);
-          a.xs[(int64_t)t * nb + j] = (uint8_t)s;
-        }
+      for (int i = 0; i < 4; ++i) {
+        raw[i] = v0[i];
+        raw[4 + i] = v1[i];
       }
-    if (blockIdx.x == 0 && tid == 0) *a.gsa = gsa;
+      quant_block16(raw, gsa, c0, c1, sb);
+      *reinterpret_cast<uint2*>(a.xc + qblock * 8) = make_uint2(c0, c1);
+      a.xs[qblock] = (uint8_t)sb;
+    }
+    if (ks == 0 && tid == 0) *a.gsa = gsa;
   } else {
     gsa = *a.gsa;
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t)
-#pragma unroll
-      for (int b = 0; b < BPT; ++b) {
-        const int j = tid + b * blockDim.x;
-        xq[t][b][0] = xq[t][b][1] = 0u;
-        xsb[t][b] = 0u;
-        if (t < T && j < nb) {
-          const uint2 v = *reinterpret_cast<const uint2*>(a.xc + ((int64_t)t * nb + j) * 8);
-          xq[t][b][0] = v.x;
-          xq[t][b][1] = v.y;
-          xsb[t][b] = a.xs[(int64_t)t * nb + j];
-        }
-      }
+    if (quantizer) {
+      const uint2 v = *reinterpret_cast<const uint2*>(a.xc + qblock * 8);
+      c0 = v.x;
+      c1 = v.y;
+      sb = a.xs[qblock];
+    }
   }
+  if (tid < kDecMaxT * kDecSliceBlocks) {
+    xq_lds[qt][qkb][0] = c0;
+    xq_lds[qt][qkb][1] = c1;
+    xsb_lds[qt][qkb] = sb;
+  }
+  __syncthreads();
 
-  // Per-block dot products of exact code values, scaled by S_x * S_w (exact).
-  float acc[EPW][TMAX];
+  // Slice partials, exact: a block's contribution (sum_i qx qw) * S_x * S_w is
+  // n/4 * Mx * Mw * 2^(ex + ew) with integers n (|n| <= 2304), M <= 15 and
+  // ex, ew >= -9, i.e. an integer multiple of 2^-20 below 2^47. They are
+  // added as int64 fixed point (2^-20 units) and the 8-lane slice sum is
+  // added to the logit's device accumulator with one 64-bit atomic: integer
+  // addition is exact and associative, so the result is the exact sum in any
+  // arrival order (deterministic), scaled by gsa * gsw only at the end.
+  int64_t acc[EP][kDecMaxT];
 #pragma unroll
-  for (int p = 0; p < EPW; ++p)
+  for (int p = 0; p < EP; ++p)
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) acc[p][t] = 0.0f;
+    for (int t = 0; t < kDecMaxT; ++t) acc[p][t] = 0;
+  if (r < nkb) {
+    half8_t w0[EP], w1[EP];
+    int wm[EP], we[EP];
 #pragma unroll
-  for (int b = 0; b < BPT; ++b) {
-    const int j = tid + b * blockDim.x;
-    if (j < nb) {
+    for (int p = 0; p < EP; ++p) {
+      w0[p] = fp4x8_q(wq[p][0]);
+      w1[p] = fp4x8_q(wq[p][1]);
+      e4m3_split(wsb[p], wm[p], we[p]);
+    }
 #pragma unroll
-      for (int t = 0; t < TMAX; ++t) {
-        if (t < T) {
-          const half8_t x0 = fp4x8_q(xq[t][b][0]), x1 = fp4x8_q(xq[t][b][1]);
-          const float sx = e4m3_value(xsb[t][b]);
+    for (int t = 0; t < kDecMaxT; ++t) {
+      if (t < T) {
+        const half8_t x0 = fp4x8_q(xq_lds[t][r][0]), x1 = fp4x8_q(xq_lds[t][r][1]);
+        int xm, xe;
+        e4m3_split(xsb_lds[t][r], xm, xe);
 #pragma unroll
-          for (int p = 0; p < EPW; ++p) {
-            float d = dot8(x0, fp4x8_q(wq[p][b][0]), 0.0f);
-            d = dot8(x1, fp4x8_q(wq[p][b][1]), d);
-            acc[p][t] = fmaf(d, sx * e4m3_value(wsb[p][b]), acc[p][t]);
-          }
+        for (int p = 0; p < EP; ++p) {
+          const int n4 = (int)(4.0f * dot8(x1, w1[p], dot8(x0, w0[p], 0.0f)));  // exact
+          acc[p][t] = (int64_t)((uint64_t)(int64_t)(n4 * xm * wm[p]) << (xe + we[p] + 18));
         }
       }
     }
   }
 #pragma unroll
-  for (int t = 0; t < TMAX; ++t) {
+  for (int t = 0; t < kDecMaxT; ++t) {
     if (t < T) {
 #pragma unroll
-      for (int p = 0; p < EPW; ++p) {
-        const float v = wave_sum(acc[p][t]);
-        if (lane == 0) red[wave][p][t] = v;
+      for (int p = 0; p < EP; ++p) {
+        int64_t v = acc[p][t];
+        v += dpp_i64<kDppXor1>(v);
+        v += dpp_i64<kDppXor2>(v);
+        v += dpp_i64<kDppHalfMirror>(v);
+        const int e = q + 64 * p;
+        if (r == 0 && e < E && v != 0)
+          __hip_atomic_fetch_add(a.acc + (int64_t)t * E + e, (unsigned long long)v, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-  __syncthreads();
-  const float scale = gsa * (*a.gsw);
-  if (tid < EPW * TMAX) {
-    const int p = tid % EPW, t = tid / EPW, e = e0 + p;
-    if (t < T && e < a.E) {
-      float s = 0.0f;
-      for (int i = 0; i < nwaves; ++i) s += red[i][p][t];
-      const float L = s * scale;
-      store_coherent(a.lbuf + (int64_t)t * a.E + e, L);
-      if (a.logits_out) a.logits_out[(int64_t)t * a.E + e] = L;
-    }
-  }
 
-  if (!arrive_last(a.counter, gridDim.x, &s_last)) return;
-  for (int i = tid; i < T * a.E; i += blockDim.x) lg[i] = load_coherent(a.lbuf + i);
+  if (!arrive_last(a.counter, nslices, &s_last)) return;
+
+  // Logits: the exact fixed-point sums times 2^-20 * gsa * gsw (double, one
+  // final rounding to fp32); the accumulators go back to zero for the next call.
+  const double scale = 0x1p-20 * (double)gsa * (double)(*a.gsw);
+  for (int pi = tid; pi < T * E; pi += kDecThreads) {
+    const int64_t v = (int64_t)__hip_atomic_load(a.acc + pi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float L = (float)((double)v * scale);
+    lg[pi] = L;
+    if (a.logits_out) a.logits_out[pi] = L;
+    __hip_atomic_store(a.acc + pi, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid < E) bias_s[tid] = bias0;
   __syncthreads();
-  if (wave < T) wave_route_row<JMAX>(lg + wave * a.E, a.bias, a.E, a.k, a.routed_scale, a.idx + wave * a.k,
-                                     a.w + wave * a.k);
+  if (wave < T)  // one wavefront per token
+    wave_route_row<EP>(lg + wave * E, bias_s, E, a.k, a.routed_scale, a.idx + wave * a.k, a.w + wave * a.k,
+                       rsc[wave]);
   release_counter(a.counter);
 }
 
@@ -297,9 +323,13 @@ struct TileArgs {
 template <int JMAX>
 __global__ __launch_bounds__(256) void gate_tile_kernel(TileArgs a) {
   __shared__ float part[4][16][17];
+  __shared__ float bias_s[512];
+  __shared__ WaveRouteScratch<JMAX> rsc[4];
   __shared__ uint32_t s_last;
   extern __shared__ float lg[];  // [16][E]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float bias0 = (int)threadIdx.x < a.E ? a.bias[threadIdx.x] : 0.0f;
+  const float bias1 = (int)threadIdx.x + 256 < a.E ? a.bias[threadIdx.x + 256] : 0.0f;
   const int n = lane & 15, g = lane >> 4;
   const int col0 = blockIdx.x * 16, row0 = blockIdx.y * 16;
   const int arow = row0 + n, e = col0 + n;
@@ -346,10 +376,13 @@ __global__ __launch_bounds__(256) void gate_tile_kernel(TileArgs a) {
   if (!arrive_last(&a.counters[blockIdx.y], gridDim.x, &s_last)) return;
   const int nrows = min(16, a.T - row0);
   for (int i = threadIdx.x; i < nrows * a.E; i += 256) lg[i] = load_coherent(a.lbuf + (int64_t)row0 * a.E + i);
+  if ((int)threadIdx.x < a.E) bias_s[threadIdx.x] = bias0;
+  if ((int)threadIdx.x + 256 < a.E) bias_s[threadIdx.x + 256] = bias1;
   __syncthreads();
   for (int m = wave; m < nrows; m += 4) {
     const int64_t t = row0 + m;
-    wave_route_row<JMAX>(lg + m * a.E, a.bias, a.E, a.k, a.routed_scale, a.idx + t * a.k, a.w + t * a.k);
+    wave_route_row<JMAX>(lg + m * a.E, bias_s, a.E, a.k, a.routed_scale, a.idx + t * a.k, a.w + t * a.k,
+                         rsc[wave]);
   }
   release_counter(&a.counters[blockIdx.y]);
 }
@@ -361,8 +394,12 @@ __global__ __launch_bounds__(256) void gate_tile_kernel(TileArgs a) {
 template <int NT, int JMAX>
 __global__ __launch_bounds__(256) void gate_fused_kernel(TileArgs a) {
   extern __shared__ float lds[];  // [32][E]
+  __shared__ float bias_s[512];
+  __shared__ WaveRouteScratch<JMAX> rsc[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 31, h = lane >> 5;
+  const float bias0 = (int)threadIdx.x < a.E ? a.bias[threadIdx.x] : 0.0f;
+  const float bias1 = (int)threadIdx.x + 256 < a.E ? a.bias[threadIdx.x + 256] : 0.0f;
   const int row0 = blockIdx.x * 32;
   const int arow = row0 + r;
   const bool a_ok = arow < a.T;
@@ -406,11 +443,13 @@ __global__ __launch_bounds__(256) void gate_fused_kernel(TileArgs a) {
       }
     }
   }
+  if ((int)threadIdx.x < E) bias_s[threadIdx.x] = bias0;
+  if ((int)threadIdx.x + 256 < E) bias_s[threadIdx.x + 256] = bias1;
   __syncthreads();
   const int nrows = min(32, a.T - row0);
   for (int m = wave; m < nrows; m += 4) {
     const int64_t t = row0 + m;
-    wave_route_row<JMAX>(lds + m * E, a.bias, E, a.k, a.routed_scale, a.idx + t * a.k, a.w + t * a.k);
+    wave_route_row<JMAX>(lds + m * E, bias_s, E, a.k, a.routed_scale, a.idx + t * a.k, a.w + t * a.k, rsc[wave]);
   }
   if (a.logits_out) {
     for (int i = threadIdx.x; i < nrows * E; i += 256) a.logits_out[(int64_t)row0 * E + i] = lds[i];
@@ -433,51 +472,33 @@ const GateTuning& gate_tuning() {
   return t;
 }
 
-// Blocks per thread of the gemv kernel (0 if D is too large for it).
-static int gemv_bpt(int64_t D) {
-  const int64_t nb = D / 16;
-  for (int bpt : {1, 2, 4})
-    if ((nb + bpt - 1) / bpt <= kGemvMaxThreads) return bpt;
-  return 0;
-}
+static int decode_slices(int64_t D) { return (int)((D / 16 + kDecSliceBlocks - 1) / kDecSliceBlocks); }
 
 GateKind gate_kind(int64_t T, int64_t D) {
-  if (T <= kGemvMaxT && gemv_bpt(D) > 0) return GateKind::kGemv;
+  (void)D;
+  if (T <= kDecMaxT) return GateKind::kDecode;
   if (T <= gate_tuning().split_max_t) return GateKind::kTile;
   return GateKind::kFused;
 }
 
 size_t gate_scratch_bytes(int64_t T, int64_t D, int64_t E) {
-  return gate_kind(T, D) == GateKind::kFused ? 0 : (size_t)T * (size_t)E * sizeof(float);
-}
-
-template <int TMAX, int BPT, bool QUANT>
-static hipError_t launch_gemv_b(const GemvArgs& a, int threads, hipStream_t stream) {
-  const int j = (a.E + 63) / 64;
-  const int grid = (a.E + kGemvExperts - 1) / kGemvExperts;
-  if (j <= 1) gate_gemv_kernel<TMAX, BPT, 1, QUANT><<<grid, threads, 0, stream>>>(a);
-  else if (j <= 2) gate_gemv_kernel<TMAX, BPT, 2, QUANT><<<grid, threads, 0, stream>>>(a);
-  else if (j <= 4) gate_gemv_kernel<TMAX, BPT, 4, QUANT><<<grid, threads, 0, stream>>>(a);
-  else if (j <= 6) gate_gemv_kernel<TMAX, BPT, 6, QUANT><<<grid, threads, 0, stream>>>(a);
-  else gate_gemv_kernel<TMAX, BPT, 8, QUANT><<<grid, threads, 0, stream>>>(a);
-  return hipGetLastError();
+  switch (gate_kind(T, D)) {
+    case GateKind::kDecode: return 0;  // accumulators live in the fixed zeroed region
+    case GateKind::kTile: return (size_t)T * (size_t)E * sizeof(float);
+    default: return 0;
+  }
 }
 
 template <bool QUANT>
-static hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
-  const int bpt = gemv_bpt(a.D);
-  const int nb = a.D / 16;
-  int threads = ((nb + bpt - 1) / bpt + 63) / 64 * 64;
-  if (threads < 64 * kGemvMaxT) threads = 64 * kGemvMaxT;
-  if constexpr (QUANT) {
-    if (bpt == 1) return launch_gemv_b<kGemvMaxT, 1, true>(a, threads, stream);
-    return launch_gemv_b<kGemvMaxT, 2, true>(a, threads, stream);
-  }
-  switch (bpt) {
-    case 1: return launch_gemv_b<kGemvMaxT, 1, QUANT>(a, threads, stream);
-    case 2: return launch_gemv_b<kGemvMaxT, 2, QUANT>(a, threads, stream);
-    default: return launch_gemv_b<kGemvMaxT, 4, QUANT>(a, threads, stream);
-  }
+static hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  const int grid = decode_slices(a.D);
+  const int ep = (a.E + 63) / 64;
+  if (ep <= 1) gate_decode_kernel<1, QUANT><<<grid, kDecThreads, 0, stream>>>(a);
+  else if (ep <= 2) gate_decode_kernel<2, QUANT><<<grid, kDecThreads, 0, stream>>>(a);
+  else if (ep <= 4) gate_decode_kernel<4, QUANT><<<grid, kDecThreads, 0, stream>>>(a);
+  else if (ep <= 6) gate_decode_kernel<6, QUANT><<<grid, kDecThreads, 0, stream>>>(a);
+  else gate_decode_kernel<8, QUANT><<<grid, kDecThreads, 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 static hipError_t launch_tile(const TileArgs& a, hipStream_t stream) {
@@ -509,31 +530,28 @@ hipError_t launch_gate(const uint8_t* xc, const uint8_t* xs, const float* gsa, c
   if (T == 0) return hipSuccess;
   const GateKind kind = gate_kind(T, D);
   float* lbuf = static_cast<float*>(scratch);
-  if (kind == GateKind::kGemv) {
-    GemvArgs a{nullptr, nullptr, const_cast<uint8_t*>(xc), const_cast<uint8_t*>(xs), const_cast<float*>(gsa),
-               wc, ws, gsw, bias, rs, (int)T, (int)D, (int)E, (int)k, idx, w, lo, lbuf, counters};
-    return launch_gemv<false>(a, stream);
+  if (kind == GateKind::kDecode) {
+    DecodeArgs a{nullptr, nullptr, const_cast<uint8_t*>(xc), const_cast<uint8_t*>(xs), const_cast<float*>(gsa),
+                 wc, ws, gsw, bias, rs, (int)T, (int)D, (int)E, (int)k, idx, w, lo,
+                 reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(counters) + kCounterBytes), counters};
+    return launch_decode<false>(a, stream);
   }
   TileArgs a{xc, xs, gsa, wc, ws, gsw, bias, rs, (int)T, (int)D, (int)E, (int)k, idx, w, lo, lbuf, counters,
              (int)((D + 127) / 128)};
   return kind == GateKind::kTile ? launch_tile(a, stream) : launch_fused(a, stream);
 }
 
-// The quantizing gemv keeps every raw x block of a thread in registers: at
-// most two blocks per thread.
-bool forward_single_launch(int64_t T, int64_t D) {
-  const int bpt = gemv_bpt(D);
-  return gate_kind(T, D) == GateKind::kGemv && bpt > 0 && bpt <= 2;
-}
+bool forward_single_launch(int64_t T, int64_t D) { return gate_kind(T, D) == GateKind::kDecode; }
 
 hipError_t launch_forward_fused(const void* x, const float* gsa_override, uint8_t* xc, uint8_t* xs, float* gsa_out,
                                 const uint8_t* wc, const uint8_t* ws, const float* gsw, const float* bias, float rs,
                                 int64_t T, int64_t D, int64_t E, int64_t k, int32_t* idx, float* w, float* lo,
                                 uint32_t* counters, void* scratch, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  GemvArgs a{static_cast<const u32x4_t*>(x), gsa_override, xc, xs, gsa_out, wc, ws, gsw, bias, rs, (int)T, (int)D,
-             (int)E, (int)k, idx, w, lo, static_cast<float*>(scratch), counters};
-  return launch_gemv<true>(a, stream);
+  DecodeArgs a{static_cast<const u32x4_t*>(x), gsa_override, xc, xs, gsa_out, wc, ws, gsw, bias, rs, (int)T, (int)D,
+               (int)E, (int)k, idx, w, lo,
+               reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(counters) + kCounterBytes), counters};
+  return launch_decode<true>(a, stream);
 }
 
 }  // namespace nvr

@@ -29,6 +29,17 @@ __device__ __forceinline__ uint32_t bf16_pair_absmax(uint32_t w) {
   return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
 }
 
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// Largest |x| (15-bit magnitude pattern) over eight bf16 pairs, with packed
+// 16-bit maxima.
+__device__ __forceinline__ uint32_t bf16_block_absmax(const uint32_t* w) {
+  u16x2_t m = __builtin_bit_cast(u16x2_t, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w[i] & 0x7FFF7FFFu));
+  return max((uint32_t)m[0], (uint32_t)m[1]);
+}
+
 // Value of a non-negative E4M3FN byte (0x00..0x7E): m * 2^-9 when the
 // exponent field is 0, (8 + m) * 2^(e - 10) otherwise. Exact in fp32.
 __device__ __forceinline__ float e4m3_value(uint32_t b) {
@@ -75,8 +86,8 @@ __device__ __forceinline__ uint32_t sign_codes4(const uint32_t* w) {
 // are clamped away from the test. A key below kNearKeyLimit means "within
 // 32 fp32 ulps of such a value".
 __device__ __forceinline__ uint32_t near_grid_key(float q) {
-  const uint32_t u = __float_as_uint(fmaxf(fabsf(q), 0.2f));
-  return (u + 32u) << 11;  // low 21 mantissa bits, offset by 32 ulps
+  const uint32_t u = max(__float_as_uint(q) & 0x7FFFFFFFu, 0x3E4CCCCDu);  // |q| clamped to >= 0.2
+  return (u << 11) + (32u << 11);  // low 21 mantissa bits, offset by 32 ulps
 }
 constexpr uint32_t kNearKeyLimit = 64u << 11;
 
@@ -99,27 +110,78 @@ __device__ __forceinline__ uint32_t fp4_fast8(const uint32_t* w, float inv, uint
   return o;
 }
 
+// E4M3 byte of a non-negative fp32 p <= 448, rounded to nearest (exact ties
+// are not decided here: callers screen them out with near_scale_key). Normal
+// range: round the fp32 pattern to 3 mantissa bits (the carry rolls into the
+// exponent) and rebias 127 -> 7; subnormal range (p < 2^-6): p * 2^9 rounded.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float p) {
+  if (p >= 0x1p-6f) {
+    const uint32_t u = __float_as_uint(p);
+    return ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+  }
+  return (uint32_t)rintf(p * 512.0f);
+}
+
+// Distance key to the nearest value with at most four explicit mantissa bits
+// (every E4M3 rounding midpoint, subnormal ones included, is one). Values
+// below 1.2 * 2^-12 always round to scale 0 and are clamped away.
+__device__ __forceinline__ uint32_t near_scale_key(float p) {
+  const uint32_t u = max(__float_as_uint(p), __float_as_uint(0x1.3p-12f));  // p >= 0
+  return (u << 13) + (32u << 13);  // low 19 mantissa bits, offset by 32 ulps
+}
+constexpr uint32_t kNearScaleLimit = 64u << 13;
+
+// Exact E2M1 magnitude code of |x| / (gsa * S) for an element whose
+// approximate quotient q lies near a value v with at most two explicit
+// mantissa bits (near_grid_key). If v is a rounding threshold (the codes of
+// v(1 - 2^-10) and v(1 + 2^-10) differ), the side is decided by the sign of
+// |x| - v*S*gsa formed by one fma: v*S is exact (at most 7 significant
+// bits), and for gsa in [2^-100, 2^100] every term is a multiple of a power
+// of two far above the fp32 underflow threshold, so the rounded fma keeps the
+// exact sign (zero only for an exact tie, which goes to the even code).
+// Otherwise every quotient that close to v has v's code.
+__device__ __forceinline__ uint32_t e2m1_mag_exact(float xabs, float q, float S, float gsa) {
+  const float v = __uint_as_float((__float_as_uint(q) + 0x100000u) & ~0x1FFFFFu);
+  const uint32_t pair = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v * 0x1.ff8p-1f, v * 0x1.004p+0f, 1.0f, 0);
+  const uint32_t lo = pair & 7u, hi = (pair >> 4) & 7u;
+  if (lo == hi) return lo;
+  const float r = fmaf(-(v * S), gsa, xabs);
+  return r > 0.0f ? hi : (r < 0.0f ? lo : ((lo & 1u) ? hi : lo));
+}
+
+// Exact E4M3 scale byte of bmax / (6 gsa) for an approximate quotient p near
+// a value v with at most four explicit mantissa bits (near_scale_key); the
+// same construction with 6v (at most 7 significant bits, exact) and the
+// E4M3 midpoints as the thresholds.
+__device__ __forceinline__ uint32_t e4m3_byte_exact(float bmax, float p, float gsa) {
+  const float v = __uint_as_float((__float_as_uint(p) + 0x40000u) & ~0x7FFFFu);
+  const uint32_t lo = e4m3_from_f32(fminf(v * 0x1.ffep-1f, 448.0f));
+  const uint32_t hi = e4m3_from_f32(fminf(v * 0x1.001p+0f, 448.0f));
+  if (lo == hi) return lo;
+  const float r = fmaf(-(6.0f * v), gsa, bmax);
+  return r > 0.0f ? hi : (r < 0.0f ? lo : ((lo & 1u) ? hi : lo));
+}
+
 // Quantize one 16-element block held as eight bf16 pairs (element 2i in the
 // low half of w[i]) with global scale gsa. Produces 8 code bytes (c0 =
 // elements 0..7, c1 = elements 8..15) and the E4M3 scale byte.
 //
-// Block scale: E4M3 nearest to bmax / (6 gsa), decided in double (6 gsa is
-// exact there, the quotient is correctly rounded, and a quotient of these
-// operands can only be as close to an E4M3 midpoint as ~2^-31 relative
-// unless it equals it, so the double result rounds the same way as the
-// exact one).
-//
-// Element codes, fast path: q = x * rcp(gsa * S) is within ~4 ulps of the
-// exact quotient. The hardware FP4 conversion rounds q to nearest; this is
-// the exact answer unless q lies near a rounding threshold, which the
-// near_grid_key test detects. Blocks with such an element (rare on real
-// data), and blocks whose gsa * S is too small for an accurate fp32
-// reciprocal, are redone exactly in double, element by element.
+// For gsa in [2^-100, 2^100] (every real tensor):
+//  * block scale: p = bmax * rcp(6 gsa) is within ~3 ulps of the exact
+//    quotient; rounding it is exact unless it lies near an E4M3 midpoint
+//    (near_scale_key), where e4m3_byte_exact decides;
+//  * elements: q = x * rcp(gsa * S) is within ~4 ulps of the exact quotient;
+//    the hardware FP4 conversion (round to nearest, saturating, sign kept)
+//    is exact unless some q lies near a rounding threshold (near_grid_key),
+//    in which case the block's codes are redone with e2m1_mag_exact.
+// Outside that range (tensors of tiny or huge magnitude) every quotient is
+// formed in double: the operands' products are exact there, the division is
+// correctly rounded, and a quotient of these operands is either exactly on a
+// rounding boundary or ~2^-31 (relative) away from it, so the double result
+// rounds like the exact one.
 __device__ __forceinline__ void quant_block16(const uint32_t* w, float gsa, uint32_t& c0, uint32_t& c1,
                                               uint32_t& sbyte) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = max(m, bf16_pair_absmax(w[i]));
+  const uint32_t m = bf16_block_absmax(w);
   if (!(gsa > 0.0f)) {  // gsa == 0: all-zero tensor or zero override
     sbyte = 0;
     c0 = sign_codes4(w);
@@ -127,34 +189,48 @@ __device__ __forceinline__ void quant_block16(const uint32_t* w, float gsa, uint
     return;
   }
   const float bmax = __uint_as_float(m << 16);
-  sbyte = e4m3_round((double)bmax / (6.0 * (double)gsa));
+  const bool fast = gsa >= 0x1p-100f && gsa <= 0x1p100f;
+  if (fast) {
+    const float p = bmax * __builtin_amdgcn_rcpf(6.0f * gsa);
+    sbyte = near_scale_key(p) < kNearScaleLimit ? e4m3_byte_exact(bmax, p, gsa) : e4m3_from_f32(fminf(p, 448.0f));
+  } else {
+    sbyte = e4m3_round((double)bmax / (6.0 * (double)gsa));
+  }
   const float S = e4m3_value(sbyte);
   if (S == 0.0f) {
     c0 = sign_codes4(w);
     c1 = sign_codes4(w + 4);
     return;
   }
-  const float G = gsa * S;
-  bool exact = !(G >= 0x1p-100f);
-  if (!exact) {
-    const float inv = __builtin_amdgcn_rcpf(G);
+  if (fast) {
+    const float inv = __builtin_amdgcn_rcpf(gsa * S);
     uint32_t key = 0xFFFFFFFFu;
     c0 = fp4_fast8(w, inv, key);
     c1 = fp4_fast8(w + 4, inv, key);
-    exact = key < kNearKeyLimit;
-  }
-  if (exact) {
-    const double G64 = (double)gsa * (double)S;  // exact product
-    uint32_t out[2] = {0u, 0u};
+    if (key < kNearKeyLimit) {
+      uint32_t out[2] = {0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t lo = e2m1_round(fabs((double)bf16_lo(w[i])) / G64) | ((w[i] >> 12) & 0x8u);
-      const uint32_t hi = e2m1_round(fabs((double)bf16_hi(w[i])) / G64) | ((w[i] >> 28) & 0x8u);
-      out[i >> 2] |= (lo | (hi << 4)) << (8 * (i & 3));
+      for (int i = 0; i < 8; ++i) {
+        const float alo = fabsf(bf16_lo(w[i])), ahi = fabsf(bf16_hi(w[i]));
+        const uint32_t lo = e2m1_mag_exact(alo, alo * inv, S, gsa) | ((w[i] >> 12) & 0x8u);
+        const uint32_t hi = e2m1_mag_exact(ahi, ahi * inv, S, gsa) | ((w[i] >> 28) & 0x8u);
+        out[i >> 2] |= (lo | (hi << 4)) << (8 * (i & 3));
+      }
+      c0 = out[0];
+      c1 = out[1];
     }
-    c0 = out[0];
-    c1 = out[1];
+    return;
   }
+  const double G64 = (double)gsa * (double)S;  // exact product
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lo = e2m1_round(fabs((double)bf16_lo(w[i])) / G64) | ((w[i] >> 12) & 0x8u);
+    const uint32_t hi = e2m1_round(fabs((double)bf16_hi(w[i])) / G64) | ((w[i] >> 28) & 0x8u);
+    out[i >> 2] |= (lo | (hi << 4)) << (8 * (i & 3));
+  }
+  c0 = out[0];
+  c1 = out[1];
 }
 
 // Eight E2M1 codes (one dword) times the block scale, as fp16 (exact: a code
@@ -172,6 +248,13 @@ __device__ __forceinline__ half8_t fp4x8_to_f16(uint32_t c, _Float16 s) {
 }
 
 __device__ __forceinline__ _Float16 e4m3_f16(uint32_t b) { return (_Float16)e4m3_value(b); }
+
+// E4M3 byte (0x00..0x7E) as M * 2^e with integer M <= 15 and e in [-9, 5].
+__device__ __forceinline__ void e4m3_split(uint32_t b, int& M, int& e) {
+  const int ef = (int)((b >> 3) & 0xFu), m = (int)(b & 7u);
+  M = ef ? 8 + m : m;
+  e = ef ? ef - 10 : -9;
+}
 
 // Eight E2M1 codes as their exact fp16 values, in the hardware conversion's
 // element order (scale operand 1.0: the conversion applies only the exponent
@@ -200,12 +283,19 @@ __device__ __forceinline__ float dot8(half8_t a, half8_t b, float acc) {
 // leave every lane with its 16-lane row's result; four readlanes finish.
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <- 7-i within 8
 constexpr int kDppMirror = 0x140;      // lane i <- 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ int64_t dpp_i64(int64_t v) {
+  const int lo = dpp_i<CTRL>((int)(uint32_t)v);
+  const int hi = dpp_i<CTRL>((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
 
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, __int_as_float(dpp_i<kDppXor1>(__float_as_int(v))));
@@ -246,73 +336,160 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Order-preserving key of an fp32 selection score: larger b gives a larger
+// unsigned key, equal b equal keys (-0 is folded into +0 first). Key 0 is
+// reserved for "already chosen"; only a negative NaN could map there and it
+// is lifted to 1.
+__device__ __forceinline__ uint32_t score_key(float b) {
+  const uint32_t u = __float_as_uint(b + 0.0f);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return max(k, 1u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)dpp_i<CTRL>((int)v);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u<kDppXor1>(v));
+  v = min(v, dpp_u<kDppXor2>(v));
+  v = min(v, dpp_u<kDppHalfMirror>(v));
+  v = min(v, dpp_u<kDppMirror>(v));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return min(min(r0, r1), min(r2, r3));
+}
+
+// Max over aligned groups of GL lanes (GL a power of two up to 16); every
+// lane of a group gets the group's maximum.
+template <int GL>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  if (GL >= 2) v = max(v, dpp_u<kDppXor1>(v));
+  if (GL >= 4) v = max(v, dpp_u<kDppXor2>(v));
+  if (GL >= 8) v = max(v, dpp_u<kDppHalfMirror>(v));
+  if (GL >= 16) v = max(v, dpp_u<kDppMirror>(v));
+  return v;
+}
+
+// LDS scratch of one wavefront's router.
+template <int JMAX>
+struct WaveRouteScratch {
+  uint64_t cand[64 * JMAX + 8];
+  float cs[64 * JMAX + 8];
+  float sel_s[64];
+  int sel_i[32];
+};
+
 // Six-step routing of one token by one wavefront (commit e0f60b9f,
 // dsv4/kernels/router/__init__.py: the single-pass activation/top-k
 // epilogue; sorted output as in the selection sort of commit 04cf8ca8):
 // s = sigmoid(L); b = s + bias; the k largest b in descending order (exact
 // ties to the lower expert); gather the unbiased s of each; w = s / sum s;
-// w *= routed_scale. Lane l holds experts l, l + 64, ...; each round takes
-// the wave maximum and the lowest expert index that attains it, so the
-// chosen list comes out sorted. Lrow may point to LDS or global memory.
+// w *= routed_scale.
+//
+// Lane l holds experts l, l+64, ... (JMAX of them). Selection without k
+// serial rounds:
+//  1. every lane forms s and the order-preserving score key of its experts;
+//  2. the lanes form G >= k aligned groups; the smallest group maximum is a
+//     lower bound on the k-th largest key (the G group maxima are G >= k
+//     distinct experts at or above it), so experts below it cannot be chosen;
+//  3. the survivors (at least k, typically a few more) are compacted into LDS
+//     by ballot and each one's exact rank among them is counted: larger key
+//     first, lower expert first on equal keys, i.e. the larger (key, ~expert)
+//     pair. Survivors outrank every other expert, so that is the global rank;
+//  4. ranks below k are the chosen list, already sorted; the weights use a
+//     fixed-order (DPP tree) sum of the chosen s.
+// One wavefront, no workgroup barrier: LDS traffic of a single wave is
+// processed in order, and a compiler fence keeps the code order.
 template <int JMAX>
-__device__ __forceinline__ void wave_route_row(const float* Lrow, const float* __restrict__ bias, int E, int k,
+__device__ __forceinline__ void wave_route_row(const float* Lrow, const float* bias_lds, int E, int k,
                                                float routed_scale, int32_t* __restrict__ out_idx,
-                                               float* __restrict__ out_w) {
+                                               float* __restrict__ out_w, WaveRouteScratch<JMAX>& sc) {
   const int lane = threadIdx.x & 63;
-  float s[JMAX], b[JMAX];
-  uint32_t live = 0;
-#pragma unroll
-  for (int j = 0; j < JMAX; ++j) {
-    const int e = lane + 64 * j;
-    s[j] = 0.0f;
-    b[j] = -INFINITY;
-    if (e < E) {
-      s[j] = 1.0f / (1.0f + expf(-Lrow[e]));
-      b[j] = s[j] + bias[e];
-      live |= 1u << j;
-    }
-  }
-  int my_idx = 0;
-  float my_s = 0.0f, ssum = 0.0f;
-  for (int r = 0; r < k; ++r) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < JMAX; ++j)
-      if ((live >> j) & 1u) m = fmaxf(m, b[j]);
-    const float M = wave_max(m);
-    int win = -1;
+  float s[JMAX];
+  uint32_t key[JMAX];
+  {
+    float L[JMAX], bv[JMAX];
 #pragma unroll
     for (int j = 0; j < JMAX; ++j) {
-      if (win < 0) {
-        const uint64_t bal = __ballot(((live >> j) & 1u) && b[j] == M);
-        if (bal) win = 64 * j + (__ffsll((unsigned long long)bal) - 1);
-      }
+      const int e = min(lane + 64 * j, E - 1);
+      L[j] = Lrow[e];
+      bv[j] = bias_lds[e];
     }
-    if (win < 0) {  // only NaN scores left: take the lowest remaining expert
 #pragma unroll
-      for (int j = 0; j < JMAX; ++j) {
-        if (win < 0) {
-          const uint64_t bal = __ballot((live >> j) & 1u);
-          if (bal) win = 64 * j + (__ffsll((unsigned long long)bal) - 1);
-        }
-      }
+    for (int j = 0; j < JMAX; ++j) {
+      s[j] = __builtin_amdgcn_rcpf(1.0f + expf(-L[j]));
+      key[j] = (lane + 64 * j < E) ? score_key(s[j] + bv[j]) : 0u;
     }
-    const int wj = win >> 6, wl = win & 63;
-    float sv = 0.0f;
-#pragma unroll
-    for (int j = 0; j < JMAX; ++j)
-      if (j == wj) sv = s[j];
-    sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), wl));
-    if (lane == wl) live &= ~(1u << wj);
-    if (lane == r) {
-      my_idx = win;
-      my_s = sv;
-    }
-    ssum += sv;
   }
+  uint32_t lm = key[0];
+#pragma unroll
+  for (int j = 1; j < JMAX; ++j) lm = max(lm, key[j]);
+  // Groups of GL lanes, GL the largest power of two with 64 / GL >= k.
+  uint32_t gmax;
+  if (k <= 4) gmax = group_max_u32<16>(lm);
+  else if (k <= 8) gmax = group_max_u32<8>(lm);
+  else if (k <= 16) gmax = group_max_u32<4>(lm);
+  else if (k <= 32) gmax = group_max_u32<2>(lm);
+  else gmax = lm;
+  if (k <= 4) {  // 4 groups of 16 lanes: fold pairs of rows as well
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)gmax, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)gmax, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)gmax, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)gmax, 48);
+    const uint32_t g01 = max(r0, r1), g23 = max(r2, r3);
+    gmax = k <= 2 ? (lane < 32 ? g01 : g23) : gmax;
+    gmax = k <= 1 ? max(g01, g23) : gmax;
+  }
+  const uint32_t tau = wave_min_u32(gmax);
+
+  // Compact the survivors.
+  int C = 0;
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j) {
+    const bool cand = key[j] != 0u && key[j] >= tau;
+    const uint64_t bal = __ballot(cand);
+    if (cand) {
+      const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      sc.cand[pos] = ((uint64_t)key[j] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * j));
+      sc.cs[pos] = s[j];
+    }
+    C += (int)__popcll(bal);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // Rank of each survivor among the survivors.
+  for (int c = lane; c < ((C + 63) & ~63); c += 64) {
+    const uint64_t mine = sc.cand[min(c, C - 1)];
+    const float ms = sc.cs[min(c, C - 1)];
+    int rank = 0;
+    for (int c0 = 0; c0 < C; c0 += 8) {
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = sc.cand[c0 + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) rank += (c0 + u < C && v[u] > mine) ? 1 : 0;
+    }
+    if (c < C && rank < k) {
+      sc.sel_i[rank] = (int)(0xFFFFFFFFu - (uint32_t)mine);
+      sc.sel_s[rank] = ms;
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float sv = lane < k ? sc.sel_s[min(lane, 63)] : 0.0f;
+  const int si = sc.sel_i[min(lane, 31)];
+  const float ssum = wave_sum(sv);
   if (lane < k) {
-    out_idx[lane] = my_idx;
-    out_w[lane] = routed_scale * (my_s / ssum);
+    out_idx[lane] = si;
+    out_w[lane] = routed_scale * (sv / ssum);
   }
 }
 

@@ -23,7 +23,7 @@ int status_from(hipError_t e) { return e == hipSuccess ? ROUTER_OK : ROUTER_EHIP
 
 size_t gate_need(int64_t T, int64_t D, int64_t E) {
   if (T == 0 || nvr::gate_kind(T, D) == nvr::GateKind::kFused) return 0;
-  return nvr::kCounterBytes + nvr::gate_scratch_bytes(T, D, E);
+  return nvr::kScratchOffset + nvr::gate_scratch_bytes(T, D, E);
 }
 
 size_t quantize_need(int64_t rows, int64_t D, bool override_given) {
@@ -31,7 +31,7 @@ size_t quantize_need(int64_t rows, int64_t D, bool override_given) {
   // The single-workgroup path needs no scratch; the two-pass path keeps one
   // partial maximum per amax workgroup.
   if (override_given || nblocks <= nvr::kSingleWgMaxBlocks) return 0;
-  return nvr::kCounterBytes + nvr::quantize_scratch_bytes();
+  return nvr::kScratchOffset + nvr::quantize_scratch_bytes();
 }
 
 }  // namespace
@@ -43,7 +43,7 @@ size_t router_workspace_bytes(int64_t T, int64_t D, int64_t E, int64_t k) {
   size_t scratch = nvr::quantize_scratch_bytes();
   const size_t g = nvr::gate_scratch_bytes(T, D, E);
   if (g > scratch) scratch = g;
-  return nvr::kCounterBytes + scratch;
+  return nvr::kScratchOffset + scratch;
 }
 
 int router_workspace_init(void* workspace, size_t bytes, void* stream) {
@@ -60,7 +60,7 @@ int router_quantize(const void* x, int64_t rows, int64_t D, const float* gsa_ove
   if (gsa_override && !aligned(gsa_override, 4)) return ROUTER_EINVAL;
   const size_t need = quantize_need(rows, D, gsa_override != nullptr);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return ROUTER_EINVAL;
-  void* scratch = need > 0 ? static_cast<char*>(workspace) + nvr::kCounterBytes : nullptr;
+  void* scratch = need > 0 ? static_cast<char*>(workspace) + nvr::kScratchOffset : nullptr;
   return status_from(nvr::launch_quantize(x, rows, D, gsa_override, codes, scales, gsa_out, scratch,
                                           static_cast<hipStream_t>(stream)));
 }
@@ -96,7 +96,7 @@ int router_gate_topk(const uint8_t* x_codes, const uint8_t* x_scales, const floa
   if (st != ROUTER_OK) return st;
   const bool ws = gate_need(T, D, E) > 0;
   uint32_t* counters = ws ? static_cast<uint32_t*>(workspace) : nullptr;
-  void* scratch = ws ? static_cast<char*>(workspace) + nvr::kCounterBytes : nullptr;
+  void* scratch = ws ? static_cast<char*>(workspace) + nvr::kScratchOffset : nullptr;
   return status_from(nvr::launch_gate(x_codes, x_scales, gsa, w_codes, w_scales, gsw, bias, routed_scale, T, D, E,
                                       k, topk_idx, topk_w, logits_out, counters, scratch,
                                       static_cast<hipStream_t>(stream)));
@@ -120,17 +120,17 @@ int router_forward(const void* x, int64_t T, int64_t D, const float* gsa_overrid
   if (T > 0 && nvr::forward_single_launch(T, D)) {
     return status_from(nvr::launch_forward_fused(x, gsa_override, x_codes, x_scales, gsa_out, w_codes, w_scales, gsw,
                                                  bias, routed_scale, T, D, E, k, topk_idx, topk_w, logits_out,
-                                                 reinterpret_cast<uint32_t*>(base), base + nvr::kCounterBytes, s));
+                                                 reinterpret_cast<uint32_t*>(base), base + nvr::kScratchOffset, s));
   }
   // Larger T: the quantize kernels then the gate kernels, back to back on the stream.
   hipError_t err = nvr::launch_quantize(x, T, D, gsa_override, x_codes, x_scales, gsa_out,
-                                        qneed > 0 ? base + nvr::kCounterBytes : nullptr, s);
+                                        qneed > 0 ? base + nvr::kScratchOffset : nullptr, s);
   if (err != hipSuccess) return ROUTER_EHIP;
   const bool ws = gate_need(T, D, E) > 0;
   return status_from(nvr::launch_gate(x_codes, x_scales, gsa_out, w_codes, w_scales, gsw, bias, routed_scale, T, D,
                                       E, k, topk_idx, topk_w, logits_out,
                                       ws ? reinterpret_cast<uint32_t*>(base) : nullptr,
-                                      ws ? base + nvr::kCounterBytes : nullptr, s));
+                                      ws ? base + nvr::kScratchOffset : nullptr, s));
 }
 
 const char* router_status_string(int status) {
