@@ -388,71 +388,192 @@ __global__ __launch_bounds__(256) void gate_tile_kernel(TileArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fused: prefill-size T. One workgroup per 32 tokens and all E experts. Wave
-// w owns expert tiles w, w+4, ... (32 experts each).
+// fused (prefill): one workgroup per BM tokens and all E experts, 4 waves.
+//  * B (gate weights): wave w owns expert tiles w, w+4, ... (32 experts each,
+//    NT per wave); each lane loads its 16 code bytes + 2 scale bytes per
+//    64-element K step straight into registers and converts them to the
+//    32x32x16 MFMA operand layout itself (no sharing needed, no LDS).
+//  * A (tokens): the BM x 64 tile of each K step is converted once, by the
+//    whole workgroup (one 16-byte chunk per thread), into an LDS buffer of fp16
+//    values that every wave reads with ds_read_b128.
+//  * Software pipeline: code bytes for step s+2 are loaded while step s runs
+//    its MFMAs, then step s+1 is converted behind them; two LDS buffers.
+//  * Epilogue: 32 rows at a time, scaled accumulators into LDS, then the
+//    16-lanes-per-token router (four tokens per wavefront at once).
 // ---------------------------------------------------------------------------
-template <int NT, int JMAX>
-__global__ __launch_bounds__(256) void gate_fused_kernel(TileArgs a) {
-  extern __shared__ float lds[];  // [32][E]
-  __shared__ float bias_s[512];
-  __shared__ WaveRouteScratch<JMAX> rsc[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+constexpr int kPrefillThreads = 256;
+constexpr int kARowHalves = 72;  // LDS row stride of the A tile (64 values + 8 pad: fewer bank conflicts)
+
+struct StepRegs {
+  u32x4_t a;          // this thread's A chunk (16 code bytes)
+  uint32_t as;        // its 2 scale bytes
+  u32x4_t b[4];       // this lane's B chunk per expert tile
+  uint32_t bs[4];
+};
+
+template <int BM, int NT>
+__device__ __forceinline__ void prefill_load(StepRegs& R, const TileArgs& a, int row0, int wave, int lane, int step,
+                                             int nsteps) {
+  const int st = min(step, nsteps - 1);  // clamped: loads past the end re-read the last step (unused)
+  const int tid = threadIdx.x;
+  // A: thread t -> row t/2 of the tile, 32-element half t%2 of the step.
+  {
+    const int r = tid >> 1, hh = tid & 1;
+    const int64_t row = row0 + r;
+    const int64_t k0 = (int64_t)st * 64 + 32 * hh;
+    const bool ok = tid < 2 * BM && row < a.T && k0 < a.D;
+    R.a = u32x4_t{0u, 0u, 0u, 0u};
+    R.as = 0u;
+    if (ok) {
+      R.a = *reinterpret_cast<const u32x4_t*>(a.xc + row * (a.D / 2) + k0 / 2);
+      R.as = *reinterpret_cast<const uint16_t*>(a.xs + row * (a.D / 16) + k0 / 16);
+    }
+  }
   const int r = lane & 31, h = lane >> 5;
-  const float bias0 = (int)threadIdx.x < a.E ? a.bias[threadIdx.x] : 0.0f;
-  const float bias1 = (int)threadIdx.x + 256 < a.E ? a.bias[threadIdx.x + 256] : 0.0f;
-  const int row0 = blockIdx.x * 32;
-  const int arow = row0 + r;
-  const bool a_ok = arow < a.T;
-  const int D = a.D, E = a.E;
-
-  f32x16_t acc[NT];
+  const int64_t k0 = (int64_t)st * 64 + 32 * h;
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
+  for (int t = 0; t < NT; ++t) {
+    const int64_t e = (int64_t)(wave + 4 * t) * 32 + r;
+    R.b[t] = u32x4_t{0u, 0u, 0u, 0u};
+    R.bs[t] = 0u;
+    if (e < a.E && k0 < a.D) {
+      R.b[t] = *reinterpret_cast<const u32x4_t*>(a.wc + e * (a.D / 2) + k0 / 2);
+      R.bs[t] = *reinterpret_cast<const uint16_t*>(a.ws + e * (a.D / 16) + k0 / 16);
+    }
+  }
+}
 
-  for (int64_t kb = 0; kb < D; kb += 64) {
-    const int64_t k0 = kb + 32 * h;
-    const bool k_ok = k0 < D;
-    const Chunk32 ca = load_chunk(a.xc, a.xs, arow, D, k0, a_ok && k_ok);
-    const _Float16 sa0 = e4m3_f16(ca.s & 0xFFu), sa1 = e4m3_f16(ca.s >> 8);
-    const half8_t A0 = fp4x8_to_f16(ca.c[0], sa0), A1 = fp4x8_to_f16(ca.c[1], sa0);
-    const half8_t A2 = fp4x8_to_f16(ca.c[2], sa1), A3 = fp4x8_to_f16(ca.c[3], sa1);
+// The thread's A chunk, converted and stored in the LDS tile.
+template <int BM>
+__device__ __forceinline__ void prefill_store_a(const StepRegs& R, _Float16* abuf) {
+  const int tid = threadIdx.x;
+  if (tid < 2 * BM) {
+    const int r = tid >> 1, hh = tid & 1;
+    const _Float16 s0 = e4m3_f16(R.as & 0xFFu), s1 = e4m3_f16(R.as >> 8);
+    half8_t* dst = reinterpret_cast<half8_t*>(abuf + r * kARowHalves + 32 * hh);
+    dst[0] = fp4x8_to_f16(R.a[0], s0);
+    dst[1] = fp4x8_to_f16(R.a[1], s0);
+    dst[2] = fp4x8_to_f16(R.a[2], s1);
+    dst[3] = fp4x8_to_f16(R.a[3], s1);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void prefill_convert_b(const StepRegs& R, half8_t (&B)[NT][4]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const _Float16 s0 = e4m3_f16(R.bs[t] & 0xFFu), s1 = e4m3_f16(R.bs[t] >> 8);
+    B[t][0] = fp4x8_to_f16(R.b[t][0], s0);
+    B[t][1] = fp4x8_to_f16(R.b[t][1], s0);
+    B[t][2] = fp4x8_to_f16(R.b[t][2], s1);
+    B[t][3] = fp4x8_to_f16(R.b[t][3], s1);
+  }
+}
+
+template <int BM, int NT>
+__device__ __forceinline__ void prefill_mfma(const _Float16* abuf, const half8_t (&B)[NT][4], int lane,
+                                             f32x16_t (&acc)[BM / 32][NT]) {
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int rt = 0; rt < BM / 32; ++rt) {
+    const half8_t* src = reinterpret_cast<const half8_t*>(abuf + (rt * 32 + r) * kARowHalves + 32 * h);
+    half8_t A[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) A[j] = src[j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[rt][t] = mfma32(A[j], B[t][j], acc[rt][t]);
+  }
+}
+
+template <int BM, int NT, int J16>
+union PrefillLds {
+  _Float16 abuf[2][BM * kARowHalves];  // K loop: the converted A tiles
+  Row16Scratch<J16> rsc[4];            // epilogue: one router scratch per wave
+};
+
+template <int BM, int NT, int J16>
+__global__ __launch_bounds__(kPrefillThreads) void gate_fused_kernel(TileArgs a) {
+  __shared__ __attribute__((aligned(16))) PrefillLds<BM, NT, J16> u;
+  __shared__ float bias_s[512];
+  extern __shared__ float lg[];  // [32][E + 16]
+  _Float16 (&abuf)[2][BM * kARowHalves] = u.abuf;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * BM;
+  const int E = a.E;
+  const int nsteps = (a.D + 63) / 64;
+  const float bias0 = (int)threadIdx.x < E ? a.bias[threadIdx.x] : 0.0f;
+  const float bias1 = (int)threadIdx.x + 256 < E ? a.bias[threadIdx.x + 256] : 0.0f;
+
+  f32x16_t acc[BM / 32][NT];
+#pragma unroll
+  for (int rt = 0; rt < BM / 32; ++rt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rt][t][v] = 0.0f;
+
+  StepRegs R0, R1;
+  half8_t B[NT][4];
+  prefill_load<BM, NT>(R0, a, row0, wave, lane, 0, nsteps);
+  prefill_load<BM, NT>(R1, a, row0, wave, lane, 1, nsteps);
+  prefill_store_a<BM>(R0, abuf[0]);
+  prefill_convert_b<NT>(R0, B);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    // Even step s: LDS buffer 0, B from R0; R0 reloads step s+2.
+    prefill_load<BM, NT>(R0, a, row0, wave, lane, s + 2, nsteps);
+    prefill_mfma<BM, NT>(abuf[0], B, lane, acc);
+    if (s + 1 >= nsteps) break;
+    prefill_store_a<BM>(R1, abuf[1]);
+    prefill_convert_b<NT>(R1, B);
+    __syncthreads();
+    // Odd step s+1: LDS buffer 1, B from R1; R1 reloads step s+3.
+    prefill_load<BM, NT>(R1, a, row0, wave, lane, s + 3, nsteps);
+    prefill_mfma<BM, NT>(abuf[1], B, lane, acc);
+    if (s + 2 >= nsteps) break;
+    prefill_store_a<BM>(R0, abuf[0]);
+    prefill_convert_b<NT>(R0, B);
+    __syncthreads();
+  }
+
+  // Epilogue, 32 rows at a time. 32x32 accumulator layout: value v of lane
+  // (r, h) is row 8(v/4) + 4h + v%4, column r.
+  const float scale = (*a.gsa) * (*a.gsw);
+  const int ldE = E + 16;
+  if ((int)threadIdx.x < E) bias_s[threadIdx.x] = bias0;
+  if ((int)threadIdx.x + 256 < E) bias_s[threadIdx.x + 256] = bias1;
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int rt = 0; rt < BM / 32; ++rt) {
+    if (row0 + rt * 32 >= a.T) break;
+    __syncthreads();
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int e = (wave + 4 * t) * 32 + r;
-      const Chunk32 cb = load_chunk(a.wc, a.ws, e, D, k0, k_ok && e < E);
-      const _Float16 sb0 = e4m3_f16(cb.s & 0xFFu), sb1 = e4m3_f16(cb.s >> 8);
-      acc[t] = mfma32(A0, fp4x8_to_f16(cb.c[0], sb0), acc[t]);
-      acc[t] = mfma32(A1, fp4x8_to_f16(cb.c[1], sb0), acc[t]);
-      acc[t] = mfma32(A2, fp4x8_to_f16(cb.c[2], sb1), acc[t]);
-      acc[t] = mfma32(A3, fp4x8_to_f16(cb.c[3], sb1), acc[t]);
-    }
-  }
-
-  // 32x32 accumulator layout: value v of lane (r, h) is row 8(v/4) + 4h + v%4, column r.
-  const float scale = (*a.gsa) * (*a.gsw);
+      if (e < E) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int e = (wave + 4 * t) * 32 + r;
-    if (e < E) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = 8 * (v >> 2) + 4 * h + (v & 3);
-        lds[m * E + e] = acc[t][v] * scale;
+        for (int v = 0; v < 16; ++v) lg[(8 * (v >> 2) + 4 * h + (v & 3)) * ldE + e] = acc[rt][t][v] * scale;
       }
     }
-  }
-  if ((int)threadIdx.x < E) bias_s[threadIdx.x] = bias0;
-  if ((int)threadIdx.x + 256 < E) bias_s[threadIdx.x + 256] = bias1;
-  __syncthreads();
-  const int nrows = min(32, a.T - row0);
-  for (int m = wave; m < nrows; m += 4) {
-    const int64_t t = row0 + m;
-    wave_route_row<JMAX>(lds + m * E, bias_s, E, a.k, a.routed_scale, a.idx + t * a.k, a.w + t * a.k, rsc[wave]);
-  }
-  if (a.logits_out) {
-    for (int i = threadIdx.x; i < nrows * E; i += 256) a.logits_out[(int64_t)row0 * E + i] = lds[i];
+    __syncthreads();
+    const int base = row0 + rt * 32;
+    // 32 rows: wave w routes rows 8w .. 8w+7, four at a time.
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int m = wave * 8 + half * 4 + (lane >> 4);
+      const int64_t t = base + m;
+      row16_route<J16>(lg + m * ldE, bias_s, E, a.k, a.routed_scale, t < a.T, a.idx + t * a.k, a.w + t * a.k,
+                       u.rsc[wave]);
+    }
+    if (a.logits_out) {
+      const int nrows = min(32, a.T - base);
+      for (int i = threadIdx.x; i < nrows * E; i += kPrefillThreads) {
+        const int m = i / E, e = i - m * E;
+        a.logits_out[(int64_t)(base + m) * E + e] = lg[m * ldE + e];
+      }
+    }
   }
 }
 
@@ -462,6 +583,7 @@ __global__ __launch_bounds__(256) void gate_fused_kernel(TileArgs a) {
 static GateTuning read_tuning() {
   GateTuning t;
   if (const char* v = getenv("NVR_SPLIT_MAX_T")) t.split_max_t = atoi(v);
+  if (const char* v = getenv("NVR_FUSED_BM")) t.fused_bm = atoi(v);
   if (t.split_max_t < 0) t.split_max_t = 0;
   if (t.split_max_t > 16 * kMaxCounters) t.split_max_t = 16 * kMaxCounters;
   return t;
@@ -513,15 +635,33 @@ static hipError_t launch_tile(const TileArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-static hipError_t launch_fused(const TileArgs& a, hipStream_t stream) {
-  const int grid = (a.T + 31) / 32;
-  const size_t lds = (size_t)32 * a.E * sizeof(float);
-  const int nt = (a.E + 127) / 128;
-  if (nt <= 1) gate_fused_kernel<1, 2><<<grid, 256, lds, stream>>>(a);
-  else if (nt <= 2) gate_fused_kernel<2, 4><<<grid, 256, lds, stream>>>(a);
-  else if (nt <= 3) gate_fused_kernel<3, 6><<<grid, 256, lds, stream>>>(a);
-  else gate_fused_kernel<4, 8><<<grid, 256, lds, stream>>>(a);
+template <int BM, int NT, int J16>
+static hipError_t launch_fused_t(const TileArgs& a, hipStream_t stream) {
+  const int grid = (a.T + BM - 1) / BM;
+  const size_t lds = (size_t)32 * (a.E + 16) * sizeof(float);
+  gate_fused_kernel<BM, NT, J16><<<grid, kPrefillThreads, lds, stream>>>(a);
   return hipGetLastError();
+}
+
+template <int BM>
+static hipError_t launch_fused_bm(const TileArgs& a, hipStream_t stream) {
+  const int nt = (a.E + 127) / 128;
+  if (nt <= 1) return a.E <= 64 ? launch_fused_t<BM, 1, 4>(a, stream) : launch_fused_t<BM, 1, 8>(a, stream);
+  if (nt <= 2) return launch_fused_t<BM, 2, 16>(a, stream);
+  if (nt <= 3) return launch_fused_t<BM, 3, 24>(a, stream);
+  return launch_fused_t<BM, 4, 32>(a, stream);
+}
+
+static hipError_t launch_fused(const TileArgs& a, hipStream_t stream) {
+  // Row tile: the largest of 128 / 64 / 32 that still gives every compute
+  // unit a workgroup (taller tiles reuse each converted weight for more rows).
+  // 128-row tiles only for E <= 256 (their accumulators, 16 x (E/32) fp32
+  // per lane, must stay in registers).
+  const int bm = gate_tuning().fused_bm > 0 ? gate_tuning().fused_bm
+                 : (a.T >= 128 * 256 && a.E <= 256 ? 128 : (a.T >= 64 * 256 ? 64 : 32));
+  if (bm >= 128) return launch_fused_bm<128>(a, stream);
+  if (bm >= 64) return launch_fused_bm<64>(a, stream);
+  return launch_fused_bm<32>(a, stream);
 }
 
 hipError_t launch_gate(const uint8_t* xc, const uint8_t* xs, const float* gsa, const uint8_t* wc, const uint8_t* ws,

@@ -336,6 +336,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Logistic function 1 / (1 + e^-L) from the hardware base-2 exponential and
+// reciprocal: e^-L = 2^(-L log2 e); relative error ~1e-6 for |L| <= 20 (the
+// scores it feeds are compared and summed at 1e-5). Saturates to exactly 0 and
+// 1 at the extremes.
+__device__ __forceinline__ float sigmoid_fast(float L) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * L));
+}
+
 // Order-preserving key of an fp32 selection score: larger b gives a larger
 // unsigned key, equal b equal keys (-0 is folded into +0 first). Key 0 is
 // reserved for "already chosen"; only a negative NaN could map there and it
@@ -421,7 +429,7 @@ __device__ __forceinline__ void wave_route_row(const float* Lrow, const float* b
     }
 #pragma unroll
     for (int j = 0; j < JMAX; ++j) {
-      s[j] = __builtin_amdgcn_rcpf(1.0f + expf(-L[j]));
+      s[j] = sigmoid_fast(L[j]);
       key[j] = (lane + 64 * j < E) ? score_key(s[j] + bv[j]) : 0u;
     }
   }
@@ -460,6 +468,7 @@ __device__ __forceinline__ void wave_route_row(const float* Lrow, const float* b
     }
     C += (int)__popcll(bal);
   }
+  if (lane < 8) sc.cand[C + lane] = 0ull;  // padding: ranks below nobody
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -474,7 +483,7 @@ __device__ __forceinline__ void wave_route_row(const float* Lrow, const float* b
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = sc.cand[c0 + u];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) rank += (c0 + u < C && v[u] > mine) ? 1 : 0;
+      for (int u = 0; u < 8; ++u) rank += v[u] > mine ? 1 : 0;
     }
     if (c < C && rank < k) {
       sc.sel_i[rank] = (int)(0xFFFFFFFFu - (uint32_t)mine);
@@ -489,7 +498,129 @@ __device__ __forceinline__ void wave_route_row(const float* Lrow, const float* b
   const float ssum = wave_sum(sv);
   if (lane < k) {
     out_idx[lane] = si;
-    out_w[lane] = routed_scale * (sv / ssum);
+    out_w[lane] = sv * (routed_scale * __builtin_amdgcn_rcpf(ssum));
+  }
+}
+
+// Throughput routing for many tokens: 16 lanes (one DPP row) per token, four
+// tokens per wavefront at once. Same six steps, same selection rule and the
+// same order as wave_route_row; the lower bound on the k-th key is the
+// smallest of the 16 lanes' maxima (16 groups >= k; for k > 16 no bound is
+// used). Lane l of a row holds experts l, l+16, ... (J16 of them). Each row
+// uses its own slice of `cand` (16 * J16 + 8 entries) and `sel` (32).
+template <int J16>
+struct Row16Scratch {
+  uint64_t cand[4][16 * J16 + 8];
+  float sel_s[4][32];
+  int sel_i[4][32];
+  uint32_t count[4];
+};
+
+__device__ __forceinline__ uint32_t row_min_u32(uint32_t v) {
+  v = min(v, dpp_u<kDppXor1>(v));
+  v = min(v, dpp_u<kDppXor2>(v));
+  v = min(v, dpp_u<kDppHalfMirror>(v));
+  v = min(v, dpp_u<kDppMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ float row_sum(float v) {
+  v += __int_as_float(dpp_i<kDppXor1>(__float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppXor2>(__float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppMirror>(__float_as_int(v)));
+  return v;
+}
+
+// Inclusive prefix sum over the 16 lanes of each DPP row.
+__device__ __forceinline__ int row_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  return v;
+}
+
+// Routes token `row` (LDS logits Lrow, LDS bias) if `valid`; every lane of
+// the wavefront must call it (DPP), each 16-lane row with its own token.
+template <int J16>
+__device__ __forceinline__ void row16_route(const float* Lrow, const float* bias_lds, int E, int k,
+                                            float routed_scale, bool valid, int32_t* __restrict__ out_idx,
+                                            float* __restrict__ out_w, Row16Scratch<J16>& sc) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, rq = lane >> 4;
+  uint32_t key[J16];
+  float s[J16];
+  uint32_t lm = 0u;
+#pragma unroll
+  for (int j = 0; j < J16; ++j) {
+    const int e = l16 + 16 * j;
+    const int ec = min(e, E - 1);
+    s[j] = sigmoid_fast(Lrow[ec]);
+    key[j] = (e < E && valid) ? score_key(s[j] + bias_lds[ec]) : 0u;
+    lm = max(lm, key[j]);
+  }
+  const uint32_t tau = k <= 16 ? row_min_u32(lm) : 1u;
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < J16; ++j) cnt += (key[j] != 0u && key[j] >= tau) ? 1 : 0;
+  const int incl = row_scan(cnt);
+  int pos = incl - cnt;
+#pragma unroll
+  for (int j = 0; j < J16; ++j) {
+    if (key[j] != 0u && key[j] >= tau) {
+      sc.cand[rq][pos] = ((uint64_t)key[j] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(l16 + 16 * j));
+      ++pos;
+    }
+  }
+  if (l16 == 15) sc.count[rq] = (uint32_t)incl;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int C = (int)sc.count[rq];
+  if (l16 < 8) sc.cand[rq][C + l16] = 0ull;  // padding: ranks below nobody
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // Rank of each survivor; the loop bound is the wavefront's largest count.
+  int cmax = C;
+  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 0));
+  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 16));
+  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 32));
+  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 48));
+  for (int c = l16; c < ((cmax + 15) & ~15); c += 16) {
+    const int cc = min(c, max(C - 1, 0));
+    const uint64_t mine = sc.cand[rq][cc];
+    int rank = 0;
+    for (int c0 = 0; c0 < cmax; c0 += 8) {
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = sc.cand[rq][min(c0 + u, C + 7)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) rank += (c0 + u < C && v[u] > mine) ? 1 : 0;
+    }
+    if (c < C && rank < k) {
+      const int e = (int)(0xFFFFFFFFu - (uint32_t)mine);
+      sc.sel_i[rq][rank] = e;
+      sc.sel_s[rq][rank] = sigmoid_fast(Lrow[e]);  // the same s the key was formed from
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // k <= 32: lanes l16 and l16 + 16 cover the chosen list.
+  const float s0 = l16 < k ? sc.sel_s[rq][l16] : 0.0f;
+  const float s1 = l16 + 16 < k ? sc.sel_s[rq][l16 + 16] : 0.0f;
+  const float ssum = row_sum(s0 + s1);
+  const float f = routed_scale * __builtin_amdgcn_rcpf(ssum);
+  if (valid) {
+    if (l16 < k) {
+      out_idx[l16] = sc.sel_i[rq][l16];
+      out_w[l16] = s0 * f;
+    }
+    if (l16 + 16 < k) {
+      out_idx[l16 + 16] = sc.sel_i[rq][l16 + 16];
+      out_w[l16 + 16] = s1 * f;
+    }
   }
 }
 

@@ -32,6 +32,7 @@ constexpr int kQuantMaxGrid = 8192;  // workgroups of the quantize pass
 // 32 rows and all experts, routing in the same workgroup).
 struct GateTuning {
   int split_max_t = 256;
+  int fused_bm = 0;  // 0: by T; else 32 / 64 / 128 rows per workgroup
 };
 const GateTuning& gate_tuning();
 
