@@ -1,22 +1,30 @@
 #!/usr/bin/env python3
 """Router benchmark on one MI355X: quantize + gate GEMM + top-k per step.
 
-A step is one router call: router_quantize on the step's activations, then
-router_gate_topk (gate projection and the six-step epilogue). The default
-workload is the decode router: T=1, D=7168, E=256, k=8, with 61 independent
-layer sets (token, NVFP4 gate weights, bias) cycled call by call, inputs
-resident in HBM before timing. Gate weights are quantized once at load time
-by the library itself (untimed), as the pages do for bf16 weights.
+A step is one router call, router_forward: runtime NVFP4 quantization of the
+step's bf16 activations, the block-scaled gate projection and the six-step
+routing epilogue. At T <= 4 tokens the library runs the whole call as one
+kernel launch. The default workload is the decode router: T=1, D=7168,
+E=256, k=8, with 61 independent layer sets (token, NVFP4 gate weights, bias)
+cycled call by call, inputs resident in HBM before timing. Gate weights are
+quantized once at load time by the library itself (untimed).
 
-Steps are replayed from a HIP graph (the decode loop of the pages is
-graph-captured), with the eager rate reported alongside. Kernel durations
-for the roofline come from HIP events around each launch on the launch
-stream. The CPU baseline is the oracle, timed on a bounded sample.
+The K timed steps are replayed from one HIP graph (decode loops are
+graph-captured), bracketed by HIP events recorded on the stream the graph is
+launched on; the eager rate and the two-call path (router_quantize, then
+router_gate_topk) are reported alongside. The roofline's `traffic` comes from
+the FETCH_SIZE / WRITE_SIZE counter summary committed under profiles/ and is
+null when the kernel sources have changed since it was taken. The CPU
+baseline is the oracle, timed on a bounded sample.
+
+`--copy-calibration MiB` instead times a plain device-to-device copy of that
+size (the reference kernel for scaling the byte counters).
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,6 +39,37 @@ if ROOT not in sys.path:
 METRIC = "router tokens/s (quant+gate GEMM+top-k) D=7168,E=256,k=8; µs/call at T=1"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_forward_T1_D7168_E256_k8_traffic.txt")
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources, so a stale counter summary is not reported for a changed kernel."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "nvfp4_block_scaled_06_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()
+
+
+def committed_traffic(path=TRAFFIC_FILE):
+    """HBM bytes per launch (fetch + write, copy-calibrated) from the committed counter summary, or None."""
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(msg):
@@ -94,6 +133,22 @@ def cpu_baseline(cfg, seconds):
                       f"({el:.1f} s; numpy float64, weights quantized beforehand)"}
 
 
+def copy_calibration(torch, mib, reps):
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE readings calibrate the
+    counters (reads and writes `mib` MiB per launch)."""
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)  # the runtime's device-to-device copy kernel
+    # The same bytes through an elementwise kernel (read n, write n), in case the runtime copy is not counted.
+    for _ in range(reps):
+        torch.bitwise_not(src.view(torch.int32), out=dst.view(torch.int32))
+    torch.cuda.synchronize()
+    assert torch.equal(torch.bitwise_not(src), dst)
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +158,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="time a plain device copy of this many MiB instead of the router")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the router path is single-GPU.",
@@ -110,6 +167,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration, max(args.steps, 1))
+        return
 
     from nvfp4_block_scaled_06_amd import router as rt
     from nvfp4_block_scaled_06_amd import workloads as wl
@@ -153,6 +214,7 @@ def main():
         return time.perf_counter() - t0
 
     def time_graph(step):
+        """(wall seconds, HIP-event seconds) of one replay of K captured steps."""
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -163,12 +225,16 @@ def main():
         torch.cuda.current_stream().wait_stream(s)
         g.replay()  # untimed warm replay
         torch.cuda.synchronize()
+        cur = torch.cuda.current_stream()  # replay() launches the graph on this stream
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record(cur)
         g.replay()
+        e1.record(cur)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         del g
-        return dt
+        return dt, e0.elapsed_time(e1) * 1e-3
 
     for step in (step_forward, step_two_calls):
         for i in range(W):
@@ -179,10 +245,12 @@ def main():
     eager_two = time_eager(step_two_calls)
     log(f"eager: forward {eager_fwd / K * 1e6:.2f} us/call, quantize+gate {eager_two / K * 1e6:.2f} us/call")
     graph_fwd = graph_two = None
+    ev_fwd = None
     if not args.eager:
-        graph_two = time_graph(step_two_calls)
-        graph_fwd = time_graph(step_forward)
-        log(f"graph: forward {graph_fwd / K * 1e6:.2f} us/call, quantize+gate {graph_two / K * 1e6:.2f} us/call")
+        graph_two, _ = time_graph(step_two_calls)
+        graph_fwd, ev_fwd = time_graph(step_forward)
+        log(f"graph: forward {graph_fwd / K * 1e6:.2f} us/call (events {ev_fwd / K * 1e6:.2f}), "
+            f"quantize+gate {graph_two / K * 1e6:.2f} us/call")
     timed_s = eager_fwd if graph_fwd is None else graph_fwd
 
     # Per-launch durations from HIP events on the launch stream (eager launches).
@@ -211,11 +279,15 @@ def main():
                 "kernel": "gate_fused_kernel" if c.T > 256 else "gate_tile_kernel",
                 "algorithmic": f"{gate_flops(c)} FLOP per launch"}
     else:
+        # One launch per step: the events around the timed replay give the average launch duration.
         nbytes = forward_bytes(c)
-        achieved = nbytes / tf / 1e9
+        t_launch = tf if ev_fwd is None else ev_fwd / K
+        achieved = nbytes / t_launch / 1e9
+        traffic = committed_traffic() if (c.cfg == 2 and not args.eager) else None
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                "kernel": "gate_gemv_kernel (quantizing, single launch per call)",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "kernel": "gate_decode_kernel (quantizing; the whole call is one launch)",
+                "launch_us": t_launch * 1e6,
                 "algorithmic": f"{nbytes} B per launch"}
 
     cpu = None

@@ -57,10 +57,11 @@ extern "C" {
  * call with these sizes (rows = T tokens, D hidden, E experts, k chosen).
  * One workspace sized by this function serves both calls.
  *
- * The first 16640 bytes hold arrival counters and fixed-point logit
- * accumulators that must be zero before the first call (allocate zero-filled
- * memory or call router_workspace_init); every call leaves them zero again.
- * Returns 0 for invalid sizes.
+ * The first 256 bytes hold arrival counters, which must be zero before the
+ * first call (allocate zero-filled memory or call router_workspace_init) and
+ * which every call leaves zero again; the rest is per-call scratch. Calls
+ * that share one workspace must be ordered (one stream); concurrent calls
+ * need workspaces of their own. Returns 0 for invalid sizes.
  */
 size_t router_workspace_bytes(int64_t T, int64_t D, int64_t E, int64_t k);
 

@@ -88,23 +88,34 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, u
   return *s_flag != 0u;
 }
 
+// A uniform fp32 operand in device memory, read with a vector load where the
+// call stands: the compiler would otherwise sink a scalar load of it to its
+// first use and expose a whole memory round trip there.
+__device__ __forceinline__ float load_early(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ void release_counter(uint32_t* counter) {
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
-// decode: T <= 4. The K axis is split into slices of 8 blocks (128 elements),
-// one workgroup per slice. Each workgroup reads all of x for the global max
-// (the quantizing variant; a few KB from L2), quantizes only its own slice,
-// and forms the slice's partial dot products for every expert: lane group q
-// owns experts q, q+64, ..., lane r of the group one K block, and an 8-lane
-// segmented sum gives the slice partial. The last workgroup to arrive adds
-// the slice partials in slice order and routes every token.
+// decode: T <= 4 and D <= 16384. Workgroup (g, s) owns the 16 experts of
+// group g and K slice s (64 blocks, one per lane); each of its 8 wavefronts
+// owns 2 of the experts over the whole slice. Per expert row a workgroup
+// reads 512 code bytes (four whole 128-byte lines) and 64 scale bytes, and
+// the slices of one group run on one XCD, so no weight line is fetched into
+// two L2s except at group boundaries. The quantizing variant reads all of x
+// for the global max (every workgroup, from L2), then wavefront t quantizes
+// token t's 64 slice blocks; group 0 stores the codes. Each wavefront sums
+// its exact block products over the slice and stores one partial per
+// (token, expert) with a device-coherent store; the last workgroup to arrive
+// adds the slice partials in slice order and routes every token.
 // ---------------------------------------------------------------------------
 struct DecodeArgs {
   const u32x4_t* x;           // bf16 x [T, D] (quantizing variant only)
   const float* gsa_override;  // quantizing variant only; NULL = runtime gsa
-  uint8_t* xc;                // x codes [T, D/2]: written slice by slice (quantizing) or read
+  uint8_t* xc;                // x codes [T, D/2]: written by group 0 (quantizing) or read
   uint8_t* xs;                // x scales [T, D/16]: likewise
   float* gsa;                 // [1]: written by workgroup 0 (quantizing) or read
   const uint8_t* wc;
@@ -116,43 +127,53 @@ struct DecodeArgs {
   int32_t* idx;
   float* w;
   float* logits_out;
-  unsigned long long* acc;  // [T, E] fixed-point logit accumulators (zero between calls)
+  float* part;  // [nslices, T, E] slice partials (workspace scratch)
   uint32_t* counter;
+  int nslices;  // K slices of 64 blocks
+  int nwg;      // workgroups: expert groups * nslices
 };
 
 constexpr int kDecMaxT = 4;
-constexpr int kDecThreads = 512;
-constexpr int kDecSliceBlocks = 8;   // K blocks per slice (one per lane of an 8-lane group)
-constexpr int kDecAmaxChunks = 8;    // 16-byte chunks of x per thread in the first max pass
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kDecEpw = 2;                         // experts per wavefront
+constexpr int kDecGroup = kDecWaves * kDecEpw;     // experts per workgroup
+constexpr int kDecSlice = 64;                      // K blocks per slice
+constexpr int kDecMaxSlices = 16;
+constexpr int kDecAmaxChunks = 4;                  // 16-byte chunks of x per thread in the first max pass
 
 template <int EP, bool QUANT>
 __global__ __launch_bounds__(kDecThreads) void gate_decode_kernel(DecodeArgs a) {
-  __shared__ uint32_t xq_lds[kDecMaxT][kDecSliceBlocks][2];
-  __shared__ uint32_t xsb_lds[kDecMaxT][kDecSliceBlocks];
-  __shared__ uint32_t ured[kDecThreads / 64];
-  __shared__ float lg[kDecMaxT * 512];
+  constexpr int TM = kDecMaxT;
+  __shared__ uint32_t ured[kDecWaves];
+  __shared__ uint32_t xq_lds[TM][kDecSlice][2];
+  __shared__ uint32_t xs_lds[TM][kDecSlice];
+  __shared__ float lg[TM * 512];
   __shared__ float bias_s[512];
-  __shared__ WaveRouteScratch<EP> rsc[kDecMaxT];
+  __shared__ WaveRouteScratch<EP> rsc[TM];
   __shared__ uint32_t s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = tid >> 3, r = tid & 7;
-  const int ks = blockIdx.x, nslices = gridDim.x;
-  const int nb = a.D >> 4;
-  const int kb0 = ks * kDecSliceBlocks;
-  const int nkb = min(kDecSliceBlocks, nb - kb0);
-  const int T = a.T, E = a.E;
+  const int T = a.T, E = a.E, nb = a.D >> 4;
+  // Workgroup ids go to the 8 XCDs in turn; number them so that consecutive
+  // (group, slice) pairs land on one XCD: XCD x runs pairs [x q + min(x, r),
+  // ...) of nwg = 8 q + r.
+  const int nq = a.nwg >> 3, nr = a.nwg & 7, bx = blockIdx.x & 7;
+  const int n = bx * nq + min(bx, nr) + (blockIdx.x >> 3);
+  const int g = n / a.nslices, s = n - g * a.nslices;
+  const int j = s * kDecSlice + lane;  // this lane's K block
+  const bool jok = j < nb;
   const int64_t rowc = a.D / 2;
 
-  // Bias, for the last workgroup; gate-weight blocks of this lane.
+  // Every global load is issued before the first use (predicated by lane,
+  // not by uniform branches).
   const float bias0 = tid < E ? a.bias[tid] : 0.0f;
-  uint32_t wq[EP][2], wsb[EP];
+  const float gsw = load_early(a.gsw);
+  uint32_t wq[kDecEpw][2], wsb[kDecEpw];
 #pragma unroll
-  for (int p = 0; p < EP; ++p) {
-    const int e = q + 64 * p;
-    wq[p][0] = wq[p][1] = 0u;
-    wsb[p] = 0u;
-    if (e < E && r < nkb) {
-      const int j = kb0 + r;
+  for (int p = 0; p < kDecEpw; ++p) {
+    const int e = g * kDecGroup + wave * kDecEpw + p;
+    wq[p][0] = wq[p][1] = wsb[p] = 0u;
+    if (e < E && jok) {
       const uint2 v = *reinterpret_cast<const uint2*>(a.wc + (int64_t)e * rowc + 8 * j);
       wq[p][0] = v.x;
       wq[p][1] = v.y;
@@ -160,22 +181,19 @@ __global__ __launch_bounds__(kDecThreads) void gate_decode_kernel(DecodeArgs a) 
     }
   }
 
-  // The slice's x blocks: thread (t, kb) = (tid / 8, tid % 8) for tid < 8 T.
-  const int qt = tid >> 3, qkb = tid & 7;
-  const bool quantizer = tid < T * kDecSliceBlocks && qkb < nkb;
-  const int64_t qblock = (int64_t)qt * nb + kb0 + qkb;
   float gsa;
-  uint32_t c0 = 0u, c1 = 0u, sb = 0u;
+  uint32_t xq[TM][2], xsb[TM];
   if constexpr (QUANT) {
-    // Every load is issued before the first use: the slice block this lane
-    // quantizes, and the first (usually only) pass of 16-byte chunks of x
-    // for the global max. Predicated by lane, never by a uniform branch.
-    const int n16 = T * nb * 2;
+    const float ov = a.gsa_override ? load_early(a.gsa_override) : 0.0f;
+    // Wavefront t's lanes hold token t's slice blocks; all lanes stride over x for the max.
+    const bool quantizer = wave < T && jok;
+    const int64_t qblk = (int64_t)wave * nb + j;
     u32x4_t v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
     if (quantizer) {
-      v0 = a.x[2 * qblock];
-      v1 = a.x[2 * qblock + 1];
+      v0 = a.x[2 * qblk];
+      v1 = a.x[2 * qblk + 1];
     }
+    const int n16 = T * nb * 2;
     u32x4_t xv[kDecAmaxChunks];
 #pragma unroll
     for (int c = 0; c < kDecAmaxChunks; ++c) {
@@ -187,7 +205,7 @@ __global__ __launch_bounds__(kDecThreads) void gate_decode_kernel(DecodeArgs a) 
     for (int c = 0; c < kDecAmaxChunks; ++c)
       m = max(m, max(max(bf16_pair_absmax(xv[c][0]), bf16_pair_absmax(xv[c][1])),
                      max(bf16_pair_absmax(xv[c][2]), bf16_pair_absmax(xv[c][3]))));
-    for (int i = tid + kDecAmaxChunks * kDecThreads; i < n16; i += kDecThreads) {  // very large T * D only
+    for (int i = tid + kDecAmaxChunks * kDecThreads; i < n16; i += kDecThreads) {  // T * D > 8192 only
       const u32x4_t v = a.x[i];
       m = max(m, max(max(bf16_pair_absmax(v[0]), bf16_pair_absmax(v[1])),
                      max(bf16_pair_absmax(v[2]), bf16_pair_absmax(v[3]))));
@@ -197,99 +215,99 @@ __global__ __launch_bounds__(kDecThreads) void gate_decode_kernel(DecodeArgs a) 
     __syncthreads();
     uint32_t mm = 0;
 #pragma unroll
-    for (int i = 0; i < kDecThreads / 64; ++i) mm = max(mm, ured[i]);
-    gsa = a.gsa_override ? *a.gsa_override : __uint_as_float(mm << 16) / kGsaDivisor;
-    if (quantizer) {
-      uint32_t raw[8];
+    for (int i = 0; i < kDecWaves; ++i) mm = max(mm, ured[i]);
+    gsa = a.gsa_override ? ov : __uint_as_float(mm << 16) / kGsaDivisor;
+    if (wave < T) {  // lanes past the end of K hold zero codes
+      uint32_t c0 = 0u, c1 = 0u, sb = 0u;
+      if (quantizer) {
+        uint32_t raw[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        raw[i] = v0[i];
-        raw[4 + i] = v1[i];
-      }
-      quant_block16(raw, gsa, c0, c1, sb);
-      *reinterpret_cast<uint2*>(a.xc + qblock * 8) = make_uint2(c0, c1);
-      a.xs[qblock] = (uint8_t)sb;
-    }
-    if (ks == 0 && tid == 0) *a.gsa = gsa;
-  } else {
-    gsa = *a.gsa;
-    if (quantizer) {
-      const uint2 v = *reinterpret_cast<const uint2*>(a.xc + qblock * 8);
-      c0 = v.x;
-      c1 = v.y;
-      sb = a.xs[qblock];
-    }
-  }
-  if (tid < kDecMaxT * kDecSliceBlocks) {
-    xq_lds[qt][qkb][0] = c0;
-    xq_lds[qt][qkb][1] = c1;
-    xsb_lds[qt][qkb] = sb;
-  }
-  __syncthreads();
-
-  // Slice partials, exact: a block's contribution (sum_i qx qw) * S_x * S_w is
-  // n/4 * Mx * Mw * 2^(ex + ew) with integers n (|n| <= 2304), M <= 15 and
-  // ex, ew >= -9, i.e. an integer multiple of 2^-20 below 2^47. They are
-  // added as int64 fixed point (2^-20 units) and the 8-lane slice sum is
-  // added to the logit's device accumulator with one 64-bit atomic: integer
-  // addition is exact and associative, so the result is the exact sum in any
-  // arrival order (deterministic), scaled by gsa * gsw only at the end.
-  int64_t acc[EP][kDecMaxT];
-#pragma unroll
-  for (int p = 0; p < EP; ++p)
-#pragma unroll
-    for (int t = 0; t < kDecMaxT; ++t) acc[p][t] = 0;
-  if (r < nkb) {
-    half8_t w0[EP], w1[EP];
-    int wm[EP], we[EP];
-#pragma unroll
-    for (int p = 0; p < EP; ++p) {
-      w0[p] = fp4x8_q(wq[p][0]);
-      w1[p] = fp4x8_q(wq[p][1]);
-      e4m3_split(wsb[p], wm[p], we[p]);
-    }
-#pragma unroll
-    for (int t = 0; t < kDecMaxT; ++t) {
-      if (t < T) {
-        const half8_t x0 = fp4x8_q(xq_lds[t][r][0]), x1 = fp4x8_q(xq_lds[t][r][1]);
-        int xm, xe;
-        e4m3_split(xsb_lds[t][r], xm, xe);
-#pragma unroll
-        for (int p = 0; p < EP; ++p) {
-          const int n4 = (int)(4.0f * dot8(x1, w1[p], dot8(x0, w0[p], 0.0f)));  // exact
-          acc[p][t] = (int64_t)((uint64_t)(int64_t)(n4 * xm * wm[p]) << (xe + we[p] + 18));
+        for (int i = 0; i < 4; ++i) {
+          raw[i] = v0[i];
+          raw[4 + i] = v1[i];
+        }
+        quant_block16(raw, gsa, c0, c1, sb);
+        if (g == 0) {
+          *reinterpret_cast<uint2*>(a.xc + qblk * 8) = make_uint2(c0, c1);
+          a.xs[qblk] = (uint8_t)sb;
         }
       }
+      xq_lds[wave][lane][0] = c0;
+      xq_lds[wave][lane][1] = c1;
+      xs_lds[wave][lane] = sb;
     }
-  }
+    if (n == 0 && tid == 0) *a.gsa = gsa;
+    __syncthreads();
 #pragma unroll
-  for (int t = 0; t < kDecMaxT; ++t) {
-    if (t < T) {
+    for (int t = 0; t < TM; ++t) {
+      xq[t][0] = xq_lds[t][lane][0];
+      xq[t][1] = xq_lds[t][lane][1];
+      xsb[t] = xs_lds[t][lane];
+    }
+  } else {
+    gsa = load_early(a.gsa);
 #pragma unroll
-      for (int p = 0; p < EP; ++p) {
-        int64_t v = acc[p][t];
-        v += dpp_i64<kDppXor1>(v);
-        v += dpp_i64<kDppXor2>(v);
-        v += dpp_i64<kDppHalfMirror>(v);
-        const int e = q + 64 * p;
-        if (r == 0 && e < E && v != 0)
-          __hip_atomic_fetch_add(a.acc + (int64_t)t * E + e, (unsigned long long)v, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+    for (int t = 0; t < TM; ++t) {
+      const int64_t blk = (int64_t)t * nb + j;
+      xq[t][0] = xq[t][1] = xsb[t] = 0u;
+      if (t < T && jok) {
+        const uint2 v = *reinterpret_cast<const uint2*>(a.xc + blk * 8);
+        xq[t][0] = v.x;
+        xq[t][1] = v.y;
+        xsb[t] = a.xs[blk];
       }
     }
   }
 
-  if (!arrive_last(a.counter, nslices, &s_last)) return;
+  // Block products: with both operands as fp16 values q * S (exact), a
+  // block's 16 products and their sum are exact in fp32 (at most 12
+  // significant bits between the smallest product and the largest sum), so
+  // rounding starts only in the fixed-order sums over blocks and slices.
+  // Lanes past the end of K hold zero codes and add nothing.
+  half8_t w0[kDecEpw], w1[kDecEpw];
+#pragma unroll
+  for (int p = 0; p < kDecEpw; ++p) {
+    const _Float16 sw = e4m3_f16(wsb[p]);
+    w0[p] = fp4x8_to_f16(wq[p][0], sw);
+    w1[p] = fp4x8_to_f16(wq[p][1], sw);
+  }
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    if (t < T) {
+      const _Float16 sx = e4m3_f16(xsb[t]);
+      const half8_t x0 = fp4x8_to_f16(xq[t][0], sx), x1 = fp4x8_to_f16(xq[t][1], sx);
+#pragma unroll
+      for (int p = 0; p < kDecEpw; ++p) {
+        const float sum = wave_sum(dot8(x1, w1[p], dot8(x0, w0[p], 0.0f)));
+        const int e = g * kDecGroup + wave * kDecEpw + p;
+        if (lane == 0 && e < E) store_coherent(a.part + ((int64_t)s * T + t) * E + e, sum);
+      }
+    }
+  }
 
-  // Logits: the exact fixed-point sums times 2^-20 * gsa * gsw (double, one
-  // final rounding to fp32); the accumulators go back to zero for the next call.
-  const double scale = 0x1p-20 * (double)gsa * (double)(*a.gsw);
-  for (int pi = tid; pi < T * E; pi += kDecThreads) {
-    const int64_t v = (int64_t)__hip_atomic_load(a.acc + pi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float L = (float)((double)v * scale);
-    lg[pi] = L;
-    if (a.logits_out) a.logits_out[pi] = L;
-    __hip_atomic_store(a.acc + pi, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!arrive_last(a.counter, a.nwg, &s_last)) return;
+
+  // Logits: slice partials added in slice order, times gsa * gsw (double, one
+  // final rounding to fp32). Partial (q, t, e) sits at q * T * E + (t E + e).
+  // The loads of a batch of slices are issued together; slice indexes past
+  // the last one repeat it (harmless loads, not added).
+  const int npair = T * E, ns = a.nslices;
+  const double scale = (double)gsa * (double)gsw;
+  for (int i0 = 0; i0 < npair; i0 += kDecThreads) {
+    const int i = min(i0 + tid, npair - 1);
+    float sum = 0.0f;
+    for (int q0 = 0; q0 < ns; q0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = load_coherent(a.part + (min(q0 + q, ns - 1) * npair + i));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sum += q0 + q < ns ? v[q] : 0.0f;
+    }
+    if (i0 + tid < npair) {
+      const float L = (float)((double)sum * scale);
+      lg[i] = L;
+      if (a.logits_out) a.logits_out[i] = L;
+    }
   }
   if (tid < E) bias_s[tid] = bias0;
   __syncthreads();
@@ -594,18 +612,17 @@ const GateTuning& gate_tuning() {
   return t;
 }
 
-static int decode_slices(int64_t D) { return (int)((D / 16 + kDecSliceBlocks - 1) / kDecSliceBlocks); }
+static int decode_slices(int64_t D) { return (int)((D / 16 + kDecSlice - 1) / kDecSlice); }
 
 GateKind gate_kind(int64_t T, int64_t D) {
-  (void)D;
-  if (T <= kDecMaxT) return GateKind::kDecode;
+  if (T <= kDecMaxT && decode_slices(D) <= kDecMaxSlices) return GateKind::kDecode;
   if (T <= gate_tuning().split_max_t) return GateKind::kTile;
   return GateKind::kFused;
 }
 
 size_t gate_scratch_bytes(int64_t T, int64_t D, int64_t E) {
   switch (gate_kind(T, D)) {
-    case GateKind::kDecode: return 0;  // accumulators live in the fixed zeroed region
+    case GateKind::kDecode: return (size_t)decode_slices(D) * (size_t)T * (size_t)E * sizeof(float);
     case GateKind::kTile: return (size_t)T * (size_t)E * sizeof(float);
     default: return 0;
   }
@@ -613,13 +630,14 @@ size_t gate_scratch_bytes(int64_t T, int64_t D, int64_t E) {
 
 template <bool QUANT>
 static hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  const int grid = decode_slices(a.D);
+  DecodeArgs b = a;
+  b.nslices = decode_slices(a.D);
+  b.nwg = (a.E + kDecGroup - 1) / kDecGroup * b.nslices;
   const int ep = (a.E + 63) / 64;
-  if (ep <= 1) gate_decode_kernel<1, QUANT><<<grid, kDecThreads, 0, stream>>>(a);
-  else if (ep <= 2) gate_decode_kernel<2, QUANT><<<grid, kDecThreads, 0, stream>>>(a);
-  else if (ep <= 4) gate_decode_kernel<4, QUANT><<<grid, kDecThreads, 0, stream>>>(a);
-  else if (ep <= 6) gate_decode_kernel<6, QUANT><<<grid, kDecThreads, 0, stream>>>(a);
-  else gate_decode_kernel<8, QUANT><<<grid, kDecThreads, 0, stream>>>(a);
+  if (ep <= 1) gate_decode_kernel<1, QUANT><<<b.nwg, kDecThreads, 0, stream>>>(b);
+  else if (ep <= 2) gate_decode_kernel<2, QUANT><<<b.nwg, kDecThreads, 0, stream>>>(b);
+  else if (ep <= 4) gate_decode_kernel<4, QUANT><<<b.nwg, kDecThreads, 0, stream>>>(b);
+  else gate_decode_kernel<8, QUANT><<<b.nwg, kDecThreads, 0, stream>>>(b);
   return hipGetLastError();
 }
 
@@ -673,7 +691,7 @@ hipError_t launch_gate(const uint8_t* xc, const uint8_t* xs, const float* gsa, c
   if (kind == GateKind::kDecode) {
     DecodeArgs a{nullptr, nullptr, const_cast<uint8_t*>(xc), const_cast<uint8_t*>(xs), const_cast<float*>(gsa),
                  wc, ws, gsw, bias, rs, (int)T, (int)D, (int)E, (int)k, idx, w, lo,
-                 reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(counters) + kCounterBytes), counters};
+                 lbuf, counters, 0, 0};
     return launch_decode<false>(a, stream);
   }
   TileArgs a{xc, xs, gsa, wc, ws, gsw, bias, rs, (int)T, (int)D, (int)E, (int)k, idx, w, lo, lbuf, counters,
@@ -689,8 +707,7 @@ hipError_t launch_forward_fused(const void* x, const float* gsa_override, uint8_
                                 uint32_t* counters, void* scratch, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   DecodeArgs a{static_cast<const u32x4_t*>(x), gsa_override, xc, xs, gsa_out, wc, ws, gsw, bias, rs, (int)T, (int)D,
-               (int)E, (int)k, idx, w, lo,
-               reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(counters) + kCounterBytes), counters};
+               (int)E, (int)k, idx, w, lo, static_cast<float*>(scratch), counters, 0, 0};
   return launch_decode<true>(a, stream);
 }
 

@@ -41,11 +41,14 @@ __device__ __forceinline__ uint32_t bf16_block_absmax(const uint32_t* w) {
 }
 
 // Value of a non-negative E4M3FN byte (0x00..0x7E): m * 2^-9 when the
-// exponent field is 0, (8 + m) * 2^(e - 10) otherwise. Exact in fp32.
-__device__ __forceinline__ float e4m3_value(uint32_t b) {
-  const uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
-  return e ? ldexpf((float)(8u + m), (int)e - 10) : (float)m * 0x1p-9f;
+// exponent field e is 0, (8 + m) * 2^(e - 10) otherwise. Shifted left by 7,
+// the byte is the fp16 pattern of the same value times 2^-8 (fp16's
+// exponent bias is 8 more, its subnormals continue E4M3's), so one shift and
+// one exact multiply by 256 decode it.
+__device__ __forceinline__ _Float16 e4m3_f16(uint32_t b) {
+  return __builtin_bit_cast(_Float16, (uint16_t)(b << 7)) * (_Float16)256.0f;
 }
+__device__ __forceinline__ float e4m3_value(uint32_t b) { return (float)e4m3_f16(b); }
 
 // Code of the value nearest to q >= 0 on a minifloat grid with MBITS
 // mantissa bits, smallest normal exponent EMIN and largest code MAXCODE;
@@ -80,33 +83,49 @@ __device__ __forceinline__ uint32_t sign_codes4(const uint32_t* w) {
   return out;
 }
 
-// Distance key of a scaled element to the nearest value with at most two
-// explicit mantissa bits (every E2M1 rounding threshold 0.25, 0.75, 1.25,
-// 1.75, 2.5, 3.5, 5 is one). Values below 0.2 always give magnitude 0 and
-// are clamped away from the test. A key below kNearKeyLimit means "within
-// 32 fp32 ulps of such a value".
-__device__ __forceinline__ uint32_t near_grid_key(float q) {
-  const uint32_t u = max(__float_as_uint(q) & 0x7FFFFFFFu, 0x3E4CCCCDu);  // |q| clamped to >= 0.2
-  return (u << 11) + (32u << 11);  // low 21 mantissa bits, offset by 32 ulps
+// E2M1 code of one element, exact for every quotient q = |x| / (gsa S)
+// (gsa in [2^-80, 2^100], S > 0 or inv = 0), from the approximate quotient
+// qa = |x| * inv (within a few ulps of q), as the fp32 value that the
+// hardware conversion (round to nearest even, saturating) then maps to the
+// right code. Every E2M1 value and every rounding threshold (0.25, 0.75,
+// 1.25, 1.75, 2.5, 3.5, 5) has at most two explicit mantissa bits:
+//  1. v = the value nearest qa with at most two explicit mantissa bits (qa
+//     clamped to 7 first: everything above 5 saturates to 6). Between v and
+//     q there is no threshold other than v itself.
+//  2. r = |x| - v S gsa by one fma has the exact sign of q - v: v S is exact
+//     (at most 7 significant bits) and every term is a multiple of
+//     2^-31 v S gsa, far above the fp32 underflow threshold in this range.
+//     A nonzero r is at least that large, so r * 2^20 inv moves v by at
+//     least 2^-12 v.
+//  3. v is moved toward q by at most 2^-11 v: a threshold then converts to
+//     the code on q's side, an exact tie (r = 0) stays on the threshold and
+//     converts to the even code, and any other v keeps its own code.
+// The sign is copied from x last, so -0 and tiny negatives keep their sign.
+__device__ __forceinline__ float e2m1_exact_input(float x, float inv, float minv, float S, float gsa) {
+  const float xa = fabsf(x);
+  const float qa = fminf(xa * inv, 7.0f);
+  const float v = __uint_as_float((__float_as_uint(qa) + 0x100000u) & 0xFFE00000u);
+  const float r = fmaf(-(v * S), gsa, xa);
+  const float w = __builtin_amdgcn_fmed3f(fmaf(r, minv, v), v * 0x1.ffep-1f, v * 0x1.001p+0f);
+  return __uint_as_float((__float_as_uint(w) & 0x7FFFFFFFu) | (__float_as_uint(x) & 0x80000000u));
 }
-constexpr uint32_t kNearKeyLimit = 64u << 11;
 
-// One bf16 pair scaled by inv and rounded to two E2M1 codes by the hardware
-// conversion (scale operand 1.0), written into byte I of `old`: the even
-// element in the low nibble. Also folds both elements into the near-tie key.
+// One bf16 pair rounded to two E2M1 codes, written into byte I of `old`: the
+// even element in the low nibble.
 template <int I>
-__device__ __forceinline__ uint32_t fp4_fast_pair(uint32_t old, uint32_t w, float inv, uint32_t& key) {
-  const float a = bf16_lo(w) * inv, b = bf16_hi(w) * inv;
-  key = min(key, min(near_grid_key(a), near_grid_key(b)));
+__device__ __forceinline__ uint32_t fp4_exact_pair(uint32_t old, uint32_t w, float inv, float minv, float S,
+                                                   float gsa) {
+  const float a = e2m1_exact_input(bf16_lo(w), inv, minv, S, gsa);
+  const float b = e2m1_exact_input(bf16_hi(w), inv, minv, S, gsa);
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, I);
 }
 
-__device__ __forceinline__ uint32_t fp4_fast8(const uint32_t* w, float inv, uint32_t& key) {
+__device__ __forceinline__ uint32_t fp4_exact8(const uint32_t* w, float inv, float minv, float S, float gsa) {
   uint32_t o = 0;
-  o = fp4_fast_pair<0>(o, w[0], inv, key);
-  o = fp4_fast_pair<1>(o, w[1], inv, key);
-  o = fp4_fast_pair<2>(o, w[2], inv, key);
-  o = fp4_fast_pair<3>(o, w[3], inv, key);
+  o = fp4_exact_pair<0>(o, w[0], inv, minv, S, gsa);
+  o = fp4_exact_pair<1>(o, w[1], inv, minv, S, gsa);
+  o = fp4_exact_pair<2>(o, w[2], inv, minv, S, gsa);
+  o = fp4_exact_pair<3>(o, w[3], inv, minv, S, gsa);
   return o;
 }
 
@@ -123,31 +142,16 @@ __device__ __forceinline__ uint32_t e4m3_from_f32(float p) {
 }
 
 // Distance key to the nearest value with at most four explicit mantissa bits
-// (every E4M3 rounding midpoint, subnormal ones included, is one). Values
-// below 1.2 * 2^-12 always round to scale 0 and are clamped away.
+// (every E4M3 rounding midpoint, subnormal ones included, is one). p is
+// clamped to [1.2 * 2^-12, 440]: below, the scale is always 0; from 440 up
+// it is always 448 (the top midpoint 432 is far below), and neither clamp
+// value is near a four-bit value, so the block holding the tensor's max
+// (p within an ulp of 448) does not trip the test.
 __device__ __forceinline__ uint32_t near_scale_key(float p) {
-  const uint32_t u = max(__float_as_uint(p), __float_as_uint(0x1.3p-12f));  // p >= 0
+  const uint32_t u = __float_as_uint(__builtin_amdgcn_fmed3f(p, 0x1.3p-12f, 440.0f));  // p >= 0
   return (u << 13) + (32u << 13);  // low 19 mantissa bits, offset by 32 ulps
 }
 constexpr uint32_t kNearScaleLimit = 64u << 13;
-
-// Exact E2M1 magnitude code of |x| / (gsa * S) for an element whose
-// approximate quotient q lies near a value v with at most two explicit
-// mantissa bits (near_grid_key). If v is a rounding threshold (the codes of
-// v(1 - 2^-10) and v(1 + 2^-10) differ), the side is decided by the sign of
-// |x| - v*S*gsa formed by one fma: v*S is exact (at most 7 significant
-// bits), and for gsa in [2^-100, 2^100] every term is a multiple of a power
-// of two far above the fp32 underflow threshold, so the rounded fma keeps the
-// exact sign (zero only for an exact tie, which goes to the even code).
-// Otherwise every quotient that close to v has v's code.
-__device__ __forceinline__ uint32_t e2m1_mag_exact(float xabs, float q, float S, float gsa) {
-  const float v = __uint_as_float((__float_as_uint(q) + 0x100000u) & ~0x1FFFFFu);
-  const uint32_t pair = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v * 0x1.ff8p-1f, v * 0x1.004p+0f, 1.0f, 0);
-  const uint32_t lo = pair & 7u, hi = (pair >> 4) & 7u;
-  if (lo == hi) return lo;
-  const float r = fmaf(-(v * S), gsa, xabs);
-  return r > 0.0f ? hi : (r < 0.0f ? lo : ((lo & 1u) ? hi : lo));
-}
 
 // Exact E4M3 scale byte of bmax / (6 gsa) for an approximate quotient p near
 // a value v with at most four explicit mantissa bits (near_scale_key); the
@@ -166,59 +170,45 @@ __device__ __forceinline__ uint32_t e4m3_byte_exact(float bmax, float p, float g
 // low half of w[i]) with global scale gsa. Produces 8 code bytes (c0 =
 // elements 0..7, c1 = elements 8..15) and the E4M3 scale byte.
 //
-// For gsa in [2^-100, 2^100] (every real tensor):
+// For gsa in [2^-80, 2^100] (every real tensor):
 //  * block scale: p = bmax * rcp(6 gsa) is within ~3 ulps of the exact
 //    quotient; rounding it is exact unless it lies near an E4M3 midpoint
 //    (near_scale_key), where e4m3_byte_exact decides;
-//  * elements: q = x * rcp(gsa * S) is within ~4 ulps of the exact quotient;
-//    the hardware FP4 conversion (round to nearest, saturating, sign kept)
-//    is exact unless some q lies near a rounding threshold (near_grid_key),
-//    in which case the block's codes are redone with e2m1_mag_exact.
-// Outside that range (tensors of tiny or huge magnitude) every quotient is
-// formed in double: the operands' products are exact there, the division is
-// correctly rounded, and a quotient of these operands is either exactly on a
-// rounding boundary or ~2^-31 (relative) away from it, so the double result
-// rounds like the exact one.
+//  * elements: e2m1_exact_input, no data-dependent branch (with bf16
+//    inputs and E4M3 scales, quotients land exactly on E2M1 values and
+//    thresholds in a sizeable fraction of blocks, so a screened fallback
+//    would be taken by nearly every wavefront). A zero scale gives inv = 0
+//    and sign-only codes.
+// Outside that range (tensors of tiny or huge magnitude, or gsa = 0) every
+// quotient is formed in double: the operands' products are exact there, the
+// division is correctly rounded, and a quotient of these operands is either
+// exactly on a rounding boundary or ~2^-31 (relative) away from it, so the
+// double result rounds like the exact one.
 __device__ __forceinline__ void quant_block16(const uint32_t* w, float gsa, uint32_t& c0, uint32_t& c1,
                                               uint32_t& sbyte) {
   const uint32_t m = bf16_block_absmax(w);
+  const float bmax = __uint_as_float(m << 16);
+  if (gsa >= 0x1p-80f && gsa <= 0x1p100f) {
+    const float p = bmax * __builtin_amdgcn_rcpf(6.0f * gsa);
+    sbyte = near_scale_key(p) < kNearScaleLimit ? e4m3_byte_exact(bmax, p, gsa) : e4m3_from_f32(fminf(p, 448.0f));
+    const float S = e4m3_value(sbyte);
+    const float inv = S > 0.0f ? __builtin_amdgcn_rcpf(gsa * S) : 0.0f;
+    const float minv = inv * 0x1p20f;
+    c0 = fp4_exact8(w, inv, minv, S, gsa);
+    c1 = fp4_exact8(w + 4, inv, minv, S, gsa);
+    return;
+  }
   if (!(gsa > 0.0f)) {  // gsa == 0: all-zero tensor or zero override
     sbyte = 0;
     c0 = sign_codes4(w);
     c1 = sign_codes4(w + 4);
     return;
   }
-  const float bmax = __uint_as_float(m << 16);
-  const bool fast = gsa >= 0x1p-100f && gsa <= 0x1p100f;
-  if (fast) {
-    const float p = bmax * __builtin_amdgcn_rcpf(6.0f * gsa);
-    sbyte = near_scale_key(p) < kNearScaleLimit ? e4m3_byte_exact(bmax, p, gsa) : e4m3_from_f32(fminf(p, 448.0f));
-  } else {
-    sbyte = e4m3_round((double)bmax / (6.0 * (double)gsa));
-  }
+  sbyte = e4m3_round((double)bmax / (6.0 * (double)gsa));
   const float S = e4m3_value(sbyte);
   if (S == 0.0f) {
     c0 = sign_codes4(w);
     c1 = sign_codes4(w + 4);
-    return;
-  }
-  if (fast) {
-    const float inv = __builtin_amdgcn_rcpf(gsa * S);
-    uint32_t key = 0xFFFFFFFFu;
-    c0 = fp4_fast8(w, inv, key);
-    c1 = fp4_fast8(w + 4, inv, key);
-    if (key < kNearKeyLimit) {
-      uint32_t out[2] = {0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float alo = fabsf(bf16_lo(w[i])), ahi = fabsf(bf16_hi(w[i]));
-        const uint32_t lo = e2m1_mag_exact(alo, alo * inv, S, gsa) | ((w[i] >> 12) & 0x8u);
-        const uint32_t hi = e2m1_mag_exact(ahi, ahi * inv, S, gsa) | ((w[i] >> 28) & 0x8u);
-        out[i >> 2] |= (lo | (hi << 4)) << (8 * (i & 3));
-      }
-      c0 = out[0];
-      c1 = out[1];
-    }
     return;
   }
   const double G64 = (double)gsa * (double)S;  // exact product
@@ -247,29 +237,10 @@ __device__ __forceinline__ half8_t fp4x8_to_f16(uint32_t c, _Float16 s) {
   return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-__device__ __forceinline__ _Float16 e4m3_f16(uint32_t b) { return (_Float16)e4m3_value(b); }
-
-// E4M3 byte (0x00..0x7E) as M * 2^e with integer M <= 15 and e in [-9, 5].
-__device__ __forceinline__ void e4m3_split(uint32_t b, int& M, int& e) {
-  const int ef = (int)((b >> 3) & 0xFu), m = (int)(b & 7u);
-  M = ef ? 8 + m : m;
-  e = ef ? ef - 10 : -9;
-}
-
-// Eight E2M1 codes as their exact fp16 values, in the hardware conversion's
-// element order (scale operand 1.0: the conversion applies only the exponent
-// of its scale operand, so block scales are multiplied separately).
-__device__ __forceinline__ half8_t fp4x8_q(uint32_t c) {
-  const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0);
-  const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1);
-  const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2);
-  const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3);
-  return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-}
-
-// sum_i a_i * b_i over 8 fp16 pairs with fp32 accumulation. For E2M1 code
-// values every product (|q q| <= 36, a multiple of 1/4) and every partial sum
-// is exact in fp32.
+// sum_i a_i * b_i over 8 fp16 pairs with fp32 accumulation. For the scaled
+// code values of one block pair (q_x S_x and q_w S_w) every product is a
+// multiple of S_x S_w / 4 below 36 S_x S_w, so products and partial sums
+// are exact in fp32.
 __device__ __forceinline__ float dot8(half8_t a, half8_t b, float acc) {
   acc = __builtin_amdgcn_fdot2(half2_t{a[0], a[1]}, half2_t{b[0], b[1]}, acc, false);
   acc = __builtin_amdgcn_fdot2(half2_t{a[2], a[3]}, half2_t{b[2], b[3]}, acc, false);
@@ -289,13 +260,6 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <- 7-i within 8
 constexpr int kDppMirror = 0x140;      // lane i <- 15-i within 16
-
-template <int CTRL>
-__device__ __forceinline__ int64_t dpp_i64(int64_t v) {
-  const int lo = dpp_i<CTRL>((int)(uint32_t)v);
-  const int hi = dpp_i<CTRL>((int)(uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-}
 
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, __int_as_float(dpp_i<kDppXor1>(__float_as_int(v))));

@@ -10,24 +10,22 @@ namespace nvr {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Workspace layout:
-//   [0, kCounterBytes)             arrival counters of the decode and tile gates;
-//   [kCounterBytes, kScratchOffset) fixed-point logit accumulators of the
-//                                   decode gate (T <= 4, E <= 512);
-//   [kScratchOffset, ...)           per-call scratch (partial maxima of the
-//                                   quantizer, the [T, E] logits of the tile gate).
-// The first two regions are zero between calls: every call that uses them
-// returns them to zero.
+//   [0, kCounterBytes)     arrival counters of the decode and tile gates:
+//                          zero between calls (every call that counts
+//                          returns its counter to zero);
+//   [kScratchOffset, ...)  per-call scratch (partial maxima of the quantizer,
+//                          the slice partials of the decode gate, the [T, E]
+//                          logits of the tile gate).
 constexpr size_t kCounterBytes = 256;
 constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(uint32_t));
-constexpr size_t kAccBytes = 4 * 512 * sizeof(unsigned long long);
-constexpr size_t kScratchOffset = kCounterBytes + kAccBytes;
+constexpr size_t kScratchOffset = kCounterBytes;
 
 constexpr int kSingleWgMaxBlocks = 2048;  // single-workgroup quantizer up to this many blocks
 constexpr int kAmaxPartials = 1024;       // workgroups of the amax pass
 constexpr int kQuantMaxGrid = 8192;  // workgroups of the quantize pass
 
-// Gate dispatch by token count: decode (T <= 4: one workgroup per K slice, the
-// last workgroup routes), tile (T <= split_max_t: 16x16 MFMA tiles, the last
+// Gate dispatch by token count: decode (T <= 4 and D <= 16384: one workgroup
+// per 16 experts and 1024-element K slice, the last workgroup routes), tile (T <= split_max_t: 16x16 MFMA tiles, the last
 // workgroup of each 16-row tile routes), fused (larger T: one workgroup per
 // 32 rows and all experts, routing in the same workgroup).
 struct GateTuning {
