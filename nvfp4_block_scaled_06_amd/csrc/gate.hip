@@ -148,8 +148,6 @@ __global__ __launch_bounds__(kDecThreads) void gate_decode_kernel(DecodeArgs a) 
   __shared__ uint32_t ured[kDecWaves];
   __shared__ uint32_t xq_lds[TM][kDecSlice][2];
   __shared__ uint32_t xs_lds[TM][kDecSlice];
-  __shared__ float lg[TM * 512];
-  __shared__ float bias_s[512];
   __shared__ WaveRouteScratch<EP> rsc[TM];
   __shared__ uint32_t s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -166,7 +164,9 @@ __global__ __launch_bounds__(kDecThreads) void gate_decode_kernel(DecodeArgs a) 
 
   // Every global load is issued before the first use (predicated by lane,
   // not by uniform branches).
-  const float bias0 = tid < E ? a.bias[tid] : 0.0f;
+  float bv[EP];  // bias of experts lane + 64 j, for the routing wavefronts
+#pragma unroll
+  for (int jj = 0; jj < EP; ++jj) bv[jj] = a.bias[min(lane + 64 * jj, E - 1)];
   const float gsw = load_early(a.gsw);
   uint32_t wq[kDecEpw][2], wsb[kDecEpw];
 #pragma unroll
@@ -185,14 +185,14 @@ __global__ __launch_bounds__(kDecThreads) void gate_decode_kernel(DecodeArgs a) 
   uint32_t xq[TM][2], xsb[TM];
   if constexpr (QUANT) {
     const float ov = a.gsa_override ? load_early(a.gsa_override) : 0.0f;
-    // Wavefront t's lanes hold token t's slice blocks; all lanes stride over x for the max.
-    const bool quantizer = wave < T && jok;
-    const int64_t qblk = (int64_t)wave * nb + j;
-    u32x4_t v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-    if (quantizer) {
-      v0 = a.x[2 * qblk];
-      v1 = a.x[2 * qblk + 1];
-    }
+    // Wavefronts 2t and 2t + 1 quantize token t's 64 slice blocks, a lane
+    // pair per block (8 elements each; the block max through one DPP
+    // exchange). All lanes stride over x for the global max.
+    const int qt = wave >> 1, qb = ((wave & 1) << 5) | (lane >> 1), qh = lane & 1;
+    const bool quantizer = qt < T && s * kDecSlice + qb < nb;
+    const int64_t qblk = (int64_t)qt * nb + s * kDecSlice + qb;
+    u32x4_t v0 = {0u, 0u, 0u, 0u};
+    if (quantizer) v0 = a.x[2 * qblk + qh];
     const int n16 = T * nb * 2;
     u32x4_t xv[kDecAmaxChunks];
 #pragma unroll
@@ -217,24 +217,21 @@ __global__ __launch_bounds__(kDecThreads) void gate_decode_kernel(DecodeArgs a) 
 #pragma unroll
     for (int i = 0; i < kDecWaves; ++i) mm = max(mm, ured[i]);
     gsa = a.gsa_override ? ov : __uint_as_float(mm << 16) / kGsaDivisor;
-    if (wave < T) {  // lanes past the end of K hold zero codes
-      uint32_t c0 = 0u, c1 = 0u, sb = 0u;
+    if (qt < T) {  // lanes past the end of K hold zero codes
+      const uint32_t raw[4] = {v0[0], v0[1], v0[2], v0[3]};
+      const uint32_t hm = bf16_words_absmax<4>(raw);
+      const BlockScale bs = block_scale(max(hm, dpp_u<kDppXor1>(hm)), gsa);
+      uint32_t c = 0u, sb = 0u;
       if (quantizer) {
-        uint32_t raw[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          raw[i] = v0[i];
-          raw[4 + i] = v1[i];
-        }
-        quant_block16(raw, gsa, c0, c1, sb);
+        c = encode8(raw, bs, gsa);
+        sb = bs.sbyte;
         if (g == 0) {
-          *reinterpret_cast<uint2*>(a.xc + qblk * 8) = make_uint2(c0, c1);
-          a.xs[qblk] = (uint8_t)sb;
+          *reinterpret_cast<uint32_t*>(a.xc + qblk * 8 + 4 * qh) = c;
+          if (qh == 0) a.xs[qblk] = (uint8_t)sb;
         }
       }
-      xq_lds[wave][lane][0] = c0;
-      xq_lds[wave][lane][1] = c1;
-      xs_lds[wave][lane] = sb;
+      xq_lds[qt][qb][qh] = c;
+      if (qh == 0) xs_lds[qt][qb] = sb;
     }
     if (n == 0 && tid == 0) *a.gsa = gsa;
     __syncthreads();
@@ -287,33 +284,38 @@ __global__ __launch_bounds__(kDecThreads) void gate_decode_kernel(DecodeArgs a) 
 
   if (!arrive_last(a.counter, a.nwg, &s_last)) return;
 
-  // Logits: slice partials added in slice order, times gsa * gsw (double, one
-  // final rounding to fp32). Partial (q, t, e) sits at q * T * E + (t E + e).
-  // The loads of a batch of slices are issued together; slice indexes past
-  // the last one repeat it (harmless loads, not added).
-  const int npair = T * E, ns = a.nslices;
-  const double scale = (double)gsa * (double)gsw;
-  for (int i0 = 0; i0 < npair; i0 += kDecThreads) {
-    const int i = min(i0 + tid, npair - 1);
-    float sum = 0.0f;
+  // Wavefront t routes token t; it reads token t's slice partials in the
+  // router's layout (lane l: experts l, l + 64, ...) and adds them in slice
+  // order, times gsa * gsw (double, one final rounding to fp32). Partial
+  // (q, t, e) sits at (q T + t) E + e. The loads of 8 slices are issued
+  // together; slice indexes past the last one repeat it (not added).
+  if (wave < T) {
+    const int t = wave, ns = a.nslices;
+    const double scale = (double)gsa * (double)gsw;
+    float sum[EP];
+#pragma unroll
+    for (int jj = 0; jj < EP; ++jj) sum[jj] = 0.0f;
     for (int q0 = 0; q0 < ns; q0 += 8) {
-      float v[8];
+      float v[8][EP];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = load_coherent(a.part + (min(q0 + q, ns - 1) * npair + i));
+      for (int q = 0; q < 8; ++q)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) sum += q0 + q < ns ? v[q] : 0.0f;
+        for (int jj = 0; jj < EP; ++jj)
+          v[q][jj] = load_coherent(a.part + (min(q0 + q, ns - 1) * T + t) * E + min(lane + 64 * jj, E - 1));
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int jj = 0; jj < EP; ++jj) sum[jj] += q0 + q < ns ? v[q][jj] : 0.0f;
     }
-    if (i0 + tid < npair) {
-      const float L = (float)((double)sum * scale);
-      lg[i] = L;
-      if (a.logits_out) a.logits_out[i] = L;
+    float L[EP];
+#pragma unroll
+    for (int jj = 0; jj < EP; ++jj) {
+      L[jj] = (float)((double)sum[jj] * scale);
+      const int e = lane + 64 * jj;
+      if (a.logits_out && e < E) a.logits_out[t * E + e] = L[jj];
     }
+    wave_route_regs<EP>(L, bv, E, a.k, a.routed_scale, a.idx + t * a.k, a.w + t * a.k, rsc[t]);
   }
-  if (tid < E) bias_s[tid] = bias0;
-  __syncthreads();
-  if (wave < T)  // one wavefront per token
-    wave_route_row<EP>(lg + wave * E, bias_s, E, a.k, a.routed_scale, a.idx + wave * a.k, a.w + wave * a.k,
-                       rsc[wave]);
   release_counter(a.counter);
 }
 

@@ -31,14 +31,16 @@ __device__ __forceinline__ uint32_t bf16_pair_absmax(uint32_t w) {
 
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
-// Largest |x| (15-bit magnitude pattern) over eight bf16 pairs, with packed
+// Largest |x| (15-bit magnitude pattern) over N bf16 pairs, with packed
 // 16-bit maxima.
-__device__ __forceinline__ uint32_t bf16_block_absmax(const uint32_t* w) {
+template <int N>
+__device__ __forceinline__ uint32_t bf16_words_absmax(const uint32_t* w) {
   u16x2_t m = __builtin_bit_cast(u16x2_t, w[0] & 0x7FFF7FFFu);
 #pragma unroll
-  for (int i = 1; i < 8; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w[i] & 0x7FFF7FFFu));
+  for (int i = 1; i < N; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w[i] & 0x7FFF7FFFu));
   return max((uint32_t)m[0], (uint32_t)m[1]);
 }
+__device__ __forceinline__ uint32_t bf16_block_absmax(const uint32_t* w) { return bf16_words_absmax<8>(w); }
 
 // Value of a non-negative E4M3FN byte (0x00..0x7E): m * 2^-9 when the
 // exponent field e is 0, (8 + m) * 2^(e - 10) otherwise. Shifted left by 7,
@@ -166,61 +168,71 @@ __device__ __forceinline__ uint32_t e4m3_byte_exact(float bmax, float p, float g
   return r > 0.0f ? hi : (r < 0.0f ? lo : ((lo & 1u) ? hi : lo));
 }
 
-// Quantize one 16-element block held as eight bf16 pairs (element 2i in the
-// low half of w[i]) with global scale gsa. Produces 8 code bytes (c0 =
-// elements 0..7, c1 = elements 8..15) and the E4M3 scale byte.
+// Block scale of a 16-element block from its bf16 absolute maximum m (the
+// bit pattern) and the global scale gsa, with what the element encoder needs.
 //
-// For gsa in [2^-80, 2^100] (every real tensor):
-//  * block scale: p = bmax * rcp(6 gsa) is within ~3 ulps of the exact
-//    quotient; rounding it is exact unless it lies near an E4M3 midpoint
-//    (near_scale_key), where e4m3_byte_exact decides;
-//  * elements: e2m1_exact_input, no data-dependent branch (with bf16
-//    inputs and E4M3 scales, quotients land exactly on E2M1 values and
-//    thresholds in a sizeable fraction of blocks, so a screened fallback
-//    would be taken by nearly every wavefront). A zero scale gives inv = 0
-//    and sign-only codes.
+// For gsa in [2^-80, 2^100] (every real tensor; `fast`):
+//  * p = bmax * rcp(6 gsa) is within ~3 ulps of the exact quotient; rounding
+//    it is exact unless it lies near an E4M3 midpoint (near_scale_key),
+//    where e4m3_byte_exact decides;
+//  * elements then take e2m1_exact_input, with no data-dependent branch
+//    (with bf16 inputs and E4M3 scales, quotients land exactly on E2M1
+//    values and thresholds in a sizeable fraction of blocks, so a screened
+//    fallback would be taken by nearly every wavefront). A zero scale gives
+//    inv = 0 and sign-only codes.
 // Outside that range (tensors of tiny or huge magnitude, or gsa = 0) every
 // quotient is formed in double: the operands' products are exact there, the
 // division is correctly rounded, and a quotient of these operands is either
 // exactly on a rounding boundary or ~2^-31 (relative) away from it, so the
 // double result rounds like the exact one.
+struct BlockScale {
+  uint32_t sbyte;
+  float S, inv, minv;
+  double G64;  // gsa * S, exact (slow path)
+  bool fast;
+};
+
+__device__ __forceinline__ BlockScale block_scale(uint32_t m, float gsa) {
+  BlockScale b;
+  const float bmax = __uint_as_float(m << 16);
+  b.fast = gsa >= 0x1p-80f && gsa <= 0x1p100f;
+  if (b.fast) {
+    const float p = bmax * __builtin_amdgcn_rcpf(6.0f * gsa);
+    b.sbyte = near_scale_key(p) < kNearScaleLimit ? e4m3_byte_exact(bmax, p, gsa) : e4m3_from_f32(fminf(p, 448.0f));
+  } else {
+    b.sbyte = gsa > 0.0f ? e4m3_round((double)bmax / (6.0 * (double)gsa)) : 0u;
+  }
+  b.S = e4m3_value(b.sbyte);
+  b.inv = (b.fast && b.S > 0.0f) ? __builtin_amdgcn_rcpf(gsa * b.S) : 0.0f;
+  b.minv = b.inv * 0x1p20f;
+  b.G64 = (double)gsa * (double)b.S;
+  return b;
+}
+
+// Codes of 8 elements (four bf16 pairs) under block scale b, packed as the
+// quantizer packs them (element 2i in the low nibble of byte i).
+__device__ __forceinline__ uint32_t encode8(const uint32_t* w, const BlockScale& b, float gsa) {
+  if (b.fast) return fp4_exact8(w, b.inv, b.minv, b.S, gsa);
+  if (b.S == 0.0f) return sign_codes4(w);
+  uint32_t out = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = e2m1_round(fabs((double)bf16_lo(w[i])) / b.G64) | ((w[i] >> 12) & 0x8u);
+    const uint32_t hi = e2m1_round(fabs((double)bf16_hi(w[i])) / b.G64) | ((w[i] >> 28) & 0x8u);
+    out |= (lo | (hi << 4)) << (8 * i);
+  }
+  return out;
+}
+
+// Quantize one 16-element block held as eight bf16 pairs (element 2i in the
+// low half of w[i]) with global scale gsa: 8 code bytes (c0 = elements 0..7,
+// c1 = elements 8..15) and the E4M3 scale byte.
 __device__ __forceinline__ void quant_block16(const uint32_t* w, float gsa, uint32_t& c0, uint32_t& c1,
                                               uint32_t& sbyte) {
-  const uint32_t m = bf16_block_absmax(w);
-  const float bmax = __uint_as_float(m << 16);
-  if (gsa >= 0x1p-80f && gsa <= 0x1p100f) {
-    const float p = bmax * __builtin_amdgcn_rcpf(6.0f * gsa);
-    sbyte = near_scale_key(p) < kNearScaleLimit ? e4m3_byte_exact(bmax, p, gsa) : e4m3_from_f32(fminf(p, 448.0f));
-    const float S = e4m3_value(sbyte);
-    const float inv = S > 0.0f ? __builtin_amdgcn_rcpf(gsa * S) : 0.0f;
-    const float minv = inv * 0x1p20f;
-    c0 = fp4_exact8(w, inv, minv, S, gsa);
-    c1 = fp4_exact8(w + 4, inv, minv, S, gsa);
-    return;
-  }
-  if (!(gsa > 0.0f)) {  // gsa == 0: all-zero tensor or zero override
-    sbyte = 0;
-    c0 = sign_codes4(w);
-    c1 = sign_codes4(w + 4);
-    return;
-  }
-  sbyte = e4m3_round((double)bmax / (6.0 * (double)gsa));
-  const float S = e4m3_value(sbyte);
-  if (S == 0.0f) {
-    c0 = sign_codes4(w);
-    c1 = sign_codes4(w + 4);
-    return;
-  }
-  const double G64 = (double)gsa * (double)S;  // exact product
-  uint32_t out[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t lo = e2m1_round(fabs((double)bf16_lo(w[i])) / G64) | ((w[i] >> 12) & 0x8u);
-    const uint32_t hi = e2m1_round(fabs((double)bf16_hi(w[i])) / G64) | ((w[i] >> 28) & 0x8u);
-    out[i >> 2] |= (lo | (hi << 4)) << (8 * (i & 3));
-  }
-  c0 = out[0];
-  c1 = out[1];
+  const BlockScale b = block_scale(bf16_block_absmax(w), gsa);
+  sbyte = b.sbyte;
+  c0 = encode8(w, b, gsa);
+  c1 = encode8(w + 4, b, gsa);
 }
 
 // Eight E2M1 codes (one dword) times the block scale, as fp16 (exact: a code
@@ -346,6 +358,8 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
   return v;
 }
 
+constexpr int kRouteFastSurvivors = 32;
+
 // LDS scratch of one wavefront's router.
 template <int JMAX>
 struct WaveRouteScratch {
@@ -377,25 +391,16 @@ struct WaveRouteScratch {
 // One wavefront, no workgroup barrier: LDS traffic of a single wave is
 // processed in order, and a compiler fence keeps the code order.
 template <int JMAX>
-__device__ __forceinline__ void wave_route_row(const float* Lrow, const float* bias_lds, int E, int k,
-                                               float routed_scale, int32_t* __restrict__ out_idx,
-                                               float* __restrict__ out_w, WaveRouteScratch<JMAX>& sc) {
+__device__ __forceinline__ void wave_route_regs(const float (&L)[JMAX], const float (&bv)[JMAX], int E, int k,
+                                                float routed_scale, int32_t* __restrict__ out_idx,
+                                                float* __restrict__ out_w, WaveRouteScratch<JMAX>& sc) {
   const int lane = threadIdx.x & 63;
   float s[JMAX];
   uint32_t key[JMAX];
-  {
-    float L[JMAX], bv[JMAX];
 #pragma unroll
-    for (int j = 0; j < JMAX; ++j) {
-      const int e = min(lane + 64 * j, E - 1);
-      L[j] = Lrow[e];
-      bv[j] = bias_lds[e];
-    }
-#pragma unroll
-    for (int j = 0; j < JMAX; ++j) {
-      s[j] = sigmoid_fast(L[j]);
-      key[j] = (lane + 64 * j < E) ? score_key(s[j] + bv[j]) : 0u;
-    }
+  for (int j = 0; j < JMAX; ++j) {
+    s[j] = sigmoid_fast(L[j]);
+    key[j] = (lane + 64 * j < E) ? score_key(s[j] + bv[j]) : 0u;
   }
   uint32_t lm = key[0];
 #pragma unroll
@@ -432,12 +437,38 @@ __device__ __forceinline__ void wave_route_row(const float* Lrow, const float* b
     }
     C += (int)__popcll(bal);
   }
+  const float rsc = routed_scale;
+  if (C <= kRouteFastSurvivors) {
+    // Usual case: every survivor is ranked against all others with one batch
+    // of LDS reads (entries past C are zero and rank below everything), the
+    // weight sum is a DPP tree over the chosen lanes, and each chosen lane
+    // stores its own output at its rank.
+    if (lane >= C && lane < kRouteFastSurvivors) sc.cand[lane] = 0ull;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint64_t all[kRouteFastSurvivors];
+#pragma unroll
+    for (int u = 0; u < kRouteFastSurvivors; ++u) all[u] = sc.cand[u];
+    const uint64_t mine = sc.cand[lane & (kRouteFastSurvivors - 1)];
+    const float ms = sc.cs[lane & (kRouteFastSurvivors - 1)];
+    int rank = 0;
+#pragma unroll
+    for (int u = 0; u < kRouteFastSurvivors; ++u) rank += all[u] > mine ? 1 : 0;
+    const bool chosen = lane < C && rank < k;
+    const float ssum = wave_sum(chosen ? ms : 0.0f);
+    if (chosen) {
+      out_idx[rank] = (int)(0xFFFFFFFFu - (uint32_t)mine);
+      out_w[rank] = ms * (rsc * __builtin_amdgcn_rcpf(ssum));
+    }
+    return;
+  }
   if (lane < 8) sc.cand[C + lane] = 0ull;  // padding: ranks below nobody
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // Rank of each survivor among the survivors.
+  // Many survivors (flat or tied scores): rank in batches of 8.
   for (int c = lane; c < ((C + 63) & ~63); c += 64) {
     const uint64_t mine = sc.cand[min(c, C - 1)];
     const float ms = sc.cs[min(c, C - 1)];
@@ -462,8 +493,24 @@ __device__ __forceinline__ void wave_route_row(const float* Lrow, const float* b
   const float ssum = wave_sum(sv);
   if (lane < k) {
     out_idx[lane] = si;
-    out_w[lane] = sv * (routed_scale * __builtin_amdgcn_rcpf(ssum));
+    out_w[lane] = sv * (rsc * __builtin_amdgcn_rcpf(ssum));
   }
+}
+
+// The same for logits and bias in LDS (lane l takes experts l, l+64, ...).
+template <int JMAX>
+__device__ __forceinline__ void wave_route_row(const float* Lrow, const float* bias_lds, int E, int k,
+                                               float routed_scale, int32_t* __restrict__ out_idx,
+                                               float* __restrict__ out_w, WaveRouteScratch<JMAX>& sc) {
+  const int lane = threadIdx.x & 63;
+  float L[JMAX], bv[JMAX];
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j) {
+    const int e = min(lane + 64 * j, E - 1);
+    L[j] = Lrow[e];
+    bv[j] = bias_lds[e];
+  }
+  wave_route_regs<JMAX>(L, bv, E, k, routed_scale, out_idx, out_w, sc);
 }
 
 // Throughput routing for many tokens: 16 lanes (one DPP row) per token, four
