@@ -57,7 +57,7 @@ extern "C" {
  * call with these sizes (rows = T tokens, D hidden, E experts, k chosen).
  * One workspace sized by this function serves both calls.
  *
- * The first 256 bytes hold arrival counters, which must be zero before the
+ * The first 4096 bytes hold arrival counters, which must be zero before the
  * first call (allocate zero-filled memory or call router_workspace_init) and
  * which every call leaves zero again; the rest is per-call scratch. Calls
  * that share one workspace must be ordered (one stream); concurrent calls

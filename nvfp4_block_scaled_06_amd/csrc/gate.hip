@@ -35,6 +35,8 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
+
 namespace nvr {
 
 __device__ __forceinline__ f32x4_t mfma16(half8_t a, half8_t b, f32x4_t c) {
@@ -42,6 +44,19 @@ __device__ __forceinline__ f32x4_t mfma16(half8_t a, half8_t b, f32x4_t c) {
 }
 __device__ __forceinline__ f32x16_t mfma32(half8_t a, half8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Compile-time loop: f(IntC<I>{}) for I = B .. E-1.
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IntC<B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // 32 elements of one row starting at element k0 (a multiple of 32): 16 code
@@ -408,193 +423,333 @@ __global__ __launch_bounds__(256) void gate_tile_kernel(TileArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fused (prefill): one workgroup per BM tokens and all E experts, 4 waves.
-//  * B (gate weights): wave w owns expert tiles w, w+4, ... (32 experts each,
-//    NT per wave); each lane loads its 16 code bytes + 2 scale bytes per
-//    64-element K step straight into registers and converts them to the
-//    32x32x16 MFMA operand layout itself (no sharing needed, no LDS).
-//  * A (tokens): the BM x 64 tile of each K step is converted once, by the
-//    whole workgroup (one 16-byte chunk per thread), into an LDS buffer of fp16
-//    values that every wave reads with ds_read_b128.
-//  * Software pipeline: code bytes for step s+2 are loaded while step s runs
-//    its MFMAs, then step s+1 is converted behind them; two LDS buffers.
-//  * Epilogue: 32 rows at a time, scaled accumulators into LDS, then the
-//    16-lanes-per-token router (four tokens per wavefront at once).
+// mfma (prefill, T > 256): workgroup tile BM tokens x 128 NTW experts, four
+// wavefronts; wavefront w owns the 32-expert tiles w, w + 4, ... of the
+// tile's expert block. K advances 128 elements per step.
+//  * A (tokens): each step's BM x 128 tile is converted once per workgroup
+//    (32 elements per thread and row) into an LDS tile of fp16 q S values,
+//    double-buffered, which every wavefront reads with ds_read_b128.
+//  * B (gate weights): each lane loads two 32-element chunks of its expert
+//    row per step (16 code bytes + 2 scale bytes each) and converts them in
+//    registers; no other wavefront needs them.
+//  * K permutation: lane (r, h) of a 32x32x16 MFMA supplies 8 K values of
+//    row/column r from group h; in step-relative K, MFMA j (0..7) takes
+//    [32h + 8j, +8) for j < 4 and [64 + 32h + 8(j - 4), +8) for j >= 4, on A
+//    and on B alike, so every product meets its partner and each K value is
+//    used once.
+//  * Loads run mma_ring() steps ahead in a register ring.
+//  * Epilogue: when the tile holds every expert, scaled accumulators go
+//    through LDS, 32 tokens at a time, into the 16-lanes-per-token router.
+//    When E is split over NCB workgroups, each stores its logits to the
+//    workspace (device-coherent) and the last of the token block's NCB
+//    workgroups to arrive loads them all and routes the block.
+// Workgroups are numbered so that the NCB expert blocks of a token block run
+// on one XCD (x fetched from HBM once, shared in its L2).
 // ---------------------------------------------------------------------------
-constexpr int kPrefillThreads = 256;
-constexpr int kARowHalves = 72;  // LDS row stride of the A tile (64 values + 8 pad: fewer bank conflicts)
+constexpr int kMmaThreads = 256;
 
-struct StepRegs {
-  u32x4_t a;          // this thread's A chunk (16 code bytes)
-  uint32_t as;        // its 2 scale bytes
-  u32x4_t b[4];       // this lane's B chunk per expert tile
-  uint32_t bs[4];
+// K steps of loads in flight: four for the small tiles, two when the
+// accumulators and weight fragments of a wide tile already need most registers.
+template <int BM, int NTW>
+constexpr int mma_ring() {
+  return (BM / 32) * NTW >= 6 ? 2 : 4;
+}
+constexpr int kMmaARow = 136;  // LDS row stride of the A tile in halves (128 values + 8 pad)
+
+struct MmaArgs {
+  TileArgs t;
+  int ncb;     // expert blocks (workgroups per token block)
+  int nwg;     // workgroups
+  int nsteps;  // 128-element K steps, rounded up to a multiple of 4 (every ring depth divides it)
 };
 
-template <int BM, int NT>
-__device__ __forceinline__ void prefill_load(StepRegs& R, const TileArgs& a, int row0, int wave, int lane, int step,
-                                             int nsteps) {
-  const int st = min(step, nsteps - 1);  // clamped: loads past the end re-read the last step (unused)
-  const int tid = threadIdx.x;
-  // A: thread t -> row t/2 of the tile, 32-element half t%2 of the step.
-  {
-    const int r = tid >> 1, hh = tid & 1;
-    const int64_t row = row0 + r;
-    const int64_t k0 = (int64_t)st * 64 + 32 * hh;
-    const bool ok = tid < 2 * BM && row < a.T && k0 < a.D;
-    R.a = u32x4_t{0u, 0u, 0u, 0u};
-    R.as = 0u;
-    if (ok) {
-      R.a = *reinterpret_cast<const u32x4_t*>(a.xc + row * (a.D / 2) + k0 / 2);
-      R.as = *reinterpret_cast<const uint16_t*>(a.xs + row * (a.D / 16) + k0 / 16);
-    }
-  }
-  const int r = lane & 31, h = lane >> 5;
-  const int64_t k0 = (int64_t)st * 64 + 32 * h;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int64_t e = (int64_t)(wave + 4 * t) * 32 + r;
-    R.b[t] = u32x4_t{0u, 0u, 0u, 0u};
-    R.bs[t] = 0u;
-    if (e < a.E && k0 < a.D) {
-      R.b[t] = *reinterpret_cast<const u32x4_t*>(a.wc + e * (a.D / 2) + k0 / 2);
-      R.bs[t] = *reinterpret_cast<const uint16_t*>(a.ws + e * (a.D / 16) + k0 / 16);
-    }
-  }
-}
-
-// The thread's A chunk, converted and stored in the LDS tile.
+// Token rows per thread in the A tile (4 threads per row): one slot per 64
+// rows; with BM = 32 only threads 0..127 have a row.
 template <int BM>
-__device__ __forceinline__ void prefill_store_a(const StepRegs& R, _Float16* abuf) {
-  const int tid = threadIdx.x;
-  if (tid < 2 * BM) {
-    const int r = tid >> 1, hh = tid & 1;
-    const _Float16 s0 = e4m3_f16(R.as & 0xFFu), s1 = e4m3_f16(R.as >> 8);
-    half8_t* dst = reinterpret_cast<half8_t*>(abuf + r * kARowHalves + 32 * hh);
-    dst[0] = fp4x8_to_f16(R.a[0], s0);
-    dst[1] = fp4x8_to_f16(R.a[1], s0);
-    dst[2] = fp4x8_to_f16(R.a[2], s1);
-    dst[3] = fp4x8_to_f16(R.a[3], s1);
-  }
+constexpr int mma_row_slots() {
+  return BM >= 64 ? BM / 64 : 1;
 }
 
-template <int NT>
-__device__ __forceinline__ void prefill_convert_b(const StepRegs& R, half8_t (&B)[NT][4]) {
+template <int BM, int NTW>
+struct MmaRegs {
+  u32x4_t a[mma_row_slots<BM>()];  // A: this thread's 32-element chunk of rows tid/4 (+ 64 i)
+  uint32_t as[mma_row_slots<BM>()];
+  u32x4_t b[NTW][2];   // B: this lane's two chunks per expert tile
+  uint32_t bs[NTW][2];
+};
+
+// Per-thread operand addresses, formed once; a step adds 64 code bytes and
+// 8 scale bytes. A chunk is loaded only if it lies inside the row (k < D)
+// and the row exists; otherwise it stays zero and adds nothing.
+template <int BM, int NTW>
+struct MmaPtrs {
+  const uint8_t* a[mma_row_slots<BM>()];
+  const uint8_t* as[mma_row_slots<BM>()];
+  bool aok[mma_row_slots<BM>()];
+  const uint8_t* b[NTW];
+  const uint8_t* bs[NTW];
+  bool bok[NTW];
+  int ka, kb;  // K offset of this thread's A chunk / this lane's first B chunk within a step
+};
+
+template <int BM, int NTW>
+__device__ __forceinline__ MmaPtrs<BM, NTW> mma_ptrs(const TileArgs& a, int row0, int col0, int wave, int lane) {
+  MmaPtrs<BM, NTW> P;
+  const int tid = threadIdx.x, q = tid & 3, r = lane & 31, h = lane >> 5;
+  const int64_t rowc = a.D / 2, rows = a.D / 16;
+  P.ka = 32 * q;
+  P.kb = 32 * h;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const _Float16 s0 = e4m3_f16(R.bs[t] & 0xFFu), s1 = e4m3_f16(R.bs[t] >> 8);
-    B[t][0] = fp4x8_to_f16(R.b[t][0], s0);
-    B[t][1] = fp4x8_to_f16(R.b[t][1], s0);
-    B[t][2] = fp4x8_to_f16(R.b[t][2], s1);
-    B[t][3] = fp4x8_to_f16(R.b[t][3], s1);
+  for (int i = 0; i < mma_row_slots<BM>(); ++i) {
+    const int64_t row = row0 + (tid >> 2) + 64 * i;
+    P.aok[i] = (tid >> 2) + 64 * i < BM && row < a.T;
+    const int64_t rr = P.aok[i] ? row : 0;
+    P.a[i] = a.xc + rr * rowc + 16 * q;
+    P.as[i] = a.xs + rr * rows + 2 * q;
+  }
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int64_t e = col0 + (wave + 4 * t) * 32 + r;
+    P.bok[t] = e < a.E;
+    const int64_t ee = P.bok[t] ? e : 0;
+    P.b[t] = a.wc + ee * rowc + 16 * h;
+    P.bs[t] = a.ws + ee * rows + 2 * h;
+  }
+  return P;
+}
+
+template <int BM, int NTW>
+__device__ __forceinline__ void mma_load(MmaRegs<BM, NTW>& R, const MmaPtrs<BM, NTW>& P, int D, int step) {
+  const int k0 = step * 128;
+#pragma unroll
+  for (int i = 0; i < mma_row_slots<BM>(); ++i) {
+    R.a[i] = u32x4_t{0u, 0u, 0u, 0u};
+    R.as[i] = 0u;
+    if (P.aok[i] && k0 + P.ka < D) {
+      R.a[i] = *reinterpret_cast<const u32x4_t*>(P.a[i] + 64 * step);
+      R.as[i] = *reinterpret_cast<const uint16_t*>(P.as[i] + 8 * step);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      R.b[t][c] = u32x4_t{0u, 0u, 0u, 0u};
+      R.bs[t][c] = 0u;
+      if (P.bok[t] && k0 + 64 * c + P.kb < D) {
+        R.b[t][c] = *reinterpret_cast<const u32x4_t*>(P.b[t] + 64 * step + 32 * c);
+        R.bs[t][c] = *reinterpret_cast<const uint16_t*>(P.bs[t] + 8 * step + 4 * c);
+      }
+    }
+}
+
+// This thread's A chunks, converted, into the LDS tile.
+template <int BM, int NTW>
+__device__ __forceinline__ void mma_store_a(const MmaRegs<BM, NTW>& R, _Float16* abuf) {
+  const int tid = threadIdx.x, q = tid & 3;
+#pragma unroll
+  for (int i = 0; i < mma_row_slots<BM>(); ++i) {
+    const int r = (tid >> 2) + 64 * i;
+    if (r >= BM) break;  // BM = 32: threads 128..255 hold no row
+    const _Float16 s0 = e4m3_f16(R.as[i] & 0xFFu), s1 = e4m3_f16(R.as[i] >> 8);
+    half8_t* dst = reinterpret_cast<half8_t*>(abuf + r * kMmaARow + 32 * q);
+    dst[0] = fp4x8_to_f16(R.a[i][0], s0);
+    dst[1] = fp4x8_to_f16(R.a[i][1], s0);
+    dst[2] = fp4x8_to_f16(R.a[i][2], s1);
+    dst[3] = fp4x8_to_f16(R.a[i][3], s1);
   }
 }
 
-template <int BM, int NT>
-__device__ __forceinline__ void prefill_mfma(const _Float16* abuf, const half8_t (&B)[NT][4], int lane,
-                                             f32x16_t (&acc)[BM / 32][NT]) {
+// Accumulator sets per output tile: two (MFMAs j < 4 and j >= 4 alternate
+// between them) when a wavefront has fewer than four tiles, so that enough
+// independent MFMAs are in flight; they are added at the end.
+template <int BM, int NTW>
+constexpr int mma_sets() {
+  return (BM / 32) * NTW < 4 ? 2 : 1;
+}
+
+// One step's MFMAs: B converted from registers, A read from the LDS tile.
+template <int BM, int NTW>
+__device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& R, const _Float16* abuf, int lane,
+                                         f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
+  constexpr int NS = mma_sets<BM, NTW>();
   const int r = lane & 31, h = lane >> 5;
+  half8_t B[NTW][8];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const _Float16 s0 = e4m3_f16(R.bs[t][c] & 0xFFu), s1 = e4m3_f16(R.bs[t][c] >> 8);
+      B[t][4 * c + 0] = fp4x8_to_f16(R.b[t][c][0], s0);
+      B[t][4 * c + 1] = fp4x8_to_f16(R.b[t][c][1], s0);
+      B[t][4 * c + 2] = fp4x8_to_f16(R.b[t][c][2], s1);
+      B[t][4 * c + 3] = fp4x8_to_f16(R.b[t][c][3], s1);
+    }
+  // A fragments one 32-row tile at a time (eight ds_read_b128 issued
+  // together), each used against every expert tile of the wavefront.
 #pragma unroll
   for (int rt = 0; rt < BM / 32; ++rt) {
-    const half8_t* src = reinterpret_cast<const half8_t*>(abuf + (rt * 32 + r) * kARowHalves + 32 * h);
-    half8_t A[4];
+    const _Float16* row = abuf + (rt * 32 + r) * kMmaARow + 32 * h;
+    half8_t A[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) A[j] = src[j];
+    for (int j = 0; j < 8; ++j) A[j] = *reinterpret_cast<const half8_t*>(row + (j < 4 ? 8 * j : 64 + 8 * (j - 4)));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[rt][t] = mfma32(A[j], B[t][j], acc[rt][t]);
+      for (int t = 0; t < NTW; ++t) {
+        f32x16_t& c = acc[NS == 2 ? (j >> 2) : 0][rt][t];
+        c = mfma32(A[j], B[t][j], c);
+      }
   }
 }
 
-template <int BM, int NT, int J16>
-union PrefillLds {
-  _Float16 abuf[2][BM * kARowHalves];  // K loop: the converted A tiles
-  Row16Scratch<J16> rsc[4];            // epilogue: one router scratch per wave
+template <int BM, int NTW, int J16>
+union MmaLds {
+  _Float16 abuf[2][BM * kMmaARow];  // K loop: the converted A tiles
+  Row16Scratch<J16> rsc[4];         // epilogue: one router scratch per wavefront
 };
 
-template <int BM, int NT, int J16>
-__global__ __launch_bounds__(kPrefillThreads) void gate_fused_kernel(TileArgs a) {
-  __shared__ __attribute__((aligned(16))) PrefillLds<BM, NT, J16> u;
-  __shared__ float bias_s[512];
-  extern __shared__ float lg[];  // [32][E + 16]
-  _Float16 (&abuf)[2][BM * kARowHalves] = u.abuf;
+// One wavefront per SIMD is the common residency (the LDS tile allows one or
+// two workgroups per compute unit), so the kernel may use the whole register
+// file rather than spill.
+template <int BM, int NTW, int J16>
+__global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gate_mfma_kernel(MmaArgs m) {
+  constexpr int ldE = 16 * J16 + 4;  // the router reads 16 J16 entries per row, 16 bytes at a time
+  static_assert(sizeof(MmaLds<BM, NTW, J16>) + (512 + 32 * ldE) * sizeof(float) + 16 <= 160 * 1024,
+                "LDS of one workgroup must fit a compute unit");
+  const TileArgs& a = m.t;
+  __shared__ __attribute__((aligned(16))) MmaLds<BM, NTW, J16> u;
+  __shared__ __attribute__((aligned(16))) float bias_s[512];
+  __shared__ __attribute__((aligned(16))) float lg[32 * ldE];  // 32 tokens' logits at a time
+  __shared__ uint32_t s_last;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row0 = blockIdx.x * BM;
   const int E = a.E;
-  const int nsteps = (a.D + 63) / 64;
+  // Token block / expert block of this workgroup (XCD-grouped numbering).
+  const int nq = m.nwg >> 3, nr = m.nwg & 7, bx = blockIdx.x & 7;
+  const int n = bx * nq + min(bx, nr) + (blockIdx.x >> 3);
+  const int rb = n / m.ncb, cb = n - rb * m.ncb;
+  const int row0 = rb * BM, col0 = cb * 128 * NTW;
+  const int nsteps = m.nsteps;
   const float bias0 = (int)threadIdx.x < E ? a.bias[threadIdx.x] : 0.0f;
   const float bias1 = (int)threadIdx.x + 256 < E ? a.bias[threadIdx.x + 256] : 0.0f;
+  const float gsa = load_early(a.gsa), gsw = load_early(a.gsw);
 
-  f32x16_t acc[BM / 32][NT];
+  constexpr int NS = mma_sets<BM, NTW>();
+  f32x16_t acc[NS][BM / 32][NTW];
 #pragma unroll
-  for (int rt = 0; rt < BM / 32; ++rt)
+  for (int q = 0; q < NS; ++q)
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int rt = 0; rt < BM / 32; ++rt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rt][t][v] = 0.0f;
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[q][rt][t][v] = 0.0f;
 
-  StepRegs R0, R1;
-  half8_t B[NT][4];
-  prefill_load<BM, NT>(R0, a, row0, wave, lane, 0, nsteps);
-  prefill_load<BM, NT>(R1, a, row0, wave, lane, 1, nsteps);
-  prefill_store_a<BM>(R0, abuf[0]);
-  prefill_convert_b<NT>(R0, B);
+  // Steps are padded to a multiple of the ring depth: padding steps load
+  // nothing (k >= D) and add zeros.
+  const MmaPtrs<BM, NTW> P = mma_ptrs<BM, NTW>(a, row0, col0, wave, lane);
+  constexpr int RING = mma_ring<BM, NTW>();
+  MmaRegs<BM, NTW> R[RING];
+#pragma unroll
+  for (int p = 0; p < RING; ++p) mma_load<BM, NTW>(R[p], P, a.D, p);
+  mma_store_a<BM, NTW>(R[0], u.abuf[0]);
   __syncthreads();
-  for (int s = 0; s < nsteps; s += 2) {
-    // Even step s: LDS buffer 0, B from R0; R0 reloads step s+2.
-    prefill_load<BM, NT>(R0, a, row0, wave, lane, s + 2, nsteps);
-    prefill_mfma<BM, NT>(abuf[0], B, lane, acc);
-    if (s + 1 >= nsteps) break;
-    prefill_store_a<BM>(R1, abuf[1]);
-    prefill_convert_b<NT>(R1, B);
-    __syncthreads();
-    // Odd step s+1: LDS buffer 1, B from R1; R1 reloads step s+3.
-    prefill_load<BM, NT>(R1, a, row0, wave, lane, s + 3, nsteps);
-    prefill_mfma<BM, NT>(abuf[1], B, lane, acc);
-    if (s + 2 >= nsteps) break;
-    prefill_store_a<BM>(R0, abuf[0]);
-    prefill_convert_b<NT>(R0, B);
-    __syncthreads();
+  for (int s0 = 0; s0 < nsteps; s0 += RING) {
+#pragma unroll
+    for (int p = 0; p < RING; ++p) {
+      mma_step<BM, NTW>(R[p], u.abuf[p & 1], lane, acc);
+      mma_store_a<BM, NTW>(R[(p + 1) % RING], u.abuf[(p + 1) & 1]);
+      mma_load<BM, NTW>(R[p], P, a.D, s0 + p + RING);
+      __syncthreads();
+    }
+  }
+  if (NS == 2) {
+#pragma unroll
+    for (int rt = 0; rt < BM / 32; ++rt)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) acc[0][rt][t] += acc[NS - 1][rt][t];
   }
 
-  // Epilogue, 32 rows at a time. 32x32 accumulator layout: value v of lane
-  // (r, h) is row 8(v/4) + 4h + v%4, column r.
-  const float scale = (*a.gsa) * (*a.gsw);
-  const int ldE = E + 16;
+  // Epilogue. 32x32 accumulator layout: value v of lane (r, h) is row
+  // 8(v/4) + 4h + v%4, column r of its tile.
+  const float scale = gsa * gsw;
+  const int r = lane & 31, h = lane >> 5;
   if ((int)threadIdx.x < E) bias_s[threadIdx.x] = bias0;
   if ((int)threadIdx.x + 256 < E) bias_s[threadIdx.x + 256] = bias1;
-  const int r = lane & 31, h = lane >> 5;
+  if (m.ncb > 1) {
+    // Split experts: store this block's logits, then the last block routes.
 #pragma unroll
-  for (int rt = 0; rt < BM / 32; ++rt) {
-    if (row0 + rt * 32 >= a.T) break;
+    for (int rt = 0; rt < BM / 32; ++rt)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const int e = col0 + (wave + 4 * t) * 32 + r;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = row0 + rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (e < E && row < a.T) {
+            const float L = acc[0][rt][t][v] * scale;
+            store_coherent(a.lbuf + row * E + e, L);
+            if (a.logits_out) a.logits_out[row * E + e] = L;
+          }
+        }
+      }
+    if (!arrive_last(&a.counters[rb], m.ncb, &s_last)) return;
+  }
+  // Passes of 32 tokens; a compile-time row tile index keeps the accumulator
+  // indexes static (a runtime loop over this body would put them in scratch).
+  auto pass = [&](auto rtc) {
+    constexpr int rt = decltype(rtc)::value;
+    const int base = row0 + rt * 32;
+    if (base >= a.T) return;  // uniform
     __syncthreads();
+    if (m.ncb > 1) {
+      // Wavefront w gathers rows w, w + 4, ...; lane l columns l, l + 64, ...
+      // All of its loads are issued before the first store.
+      const int nrows = min(32, a.T - base);
+      float v[8][J16 / 4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int e = (wave + 4 * t) * 32 + r;
-      if (e < E) {
+      for (int rr = 0; rr < 8; ++rr)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) lg[(8 * (v >> 2) + 4 * h + (v & 3)) * ldE + e] = acc[rt][t][v] * scale;
+        for (int cc = 0; cc < J16 / 4; ++cc) {
+          const int mm = wave + 4 * rr, e = lane + 64 * cc;
+          v[rr][cc] = (mm < nrows && e < E) ? load_coherent(a.lbuf + (int64_t)(base + mm) * E + e) : 0.0f;
+        }
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+        for (int cc = 0; cc < J16 / 4; ++cc) {
+          const int mm = wave + 4 * rr, e = lane + 64 * cc;
+          if (mm < nrows && e < E) lg[mm * ldE + e] = v[rr][cc];
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const int e = (wave + 4 * t) * 32 + r;
+        if (e < E) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) lg[(8 * (v >> 2) + 4 * h + (v & 3)) * ldE + e] = acc[0][rt][t][v] * scale;
+        }
       }
     }
     __syncthreads();
-    const int base = row0 + rt * 32;
-    // 32 rows: wave w routes rows 8w .. 8w+7, four at a time.
+    // 32 rows: wavefront w routes rows 8w .. 8w+7, four at a time.
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int m = wave * 8 + half * 4 + (lane >> 4);
-      const int64_t t = base + m;
-      row16_route<J16>(lg + m * ldE, bias_s, E, a.k, a.routed_scale, t < a.T, a.idx + t * a.k, a.w + t * a.k,
+      const int mm = wave * 8 + half * 4 + (lane >> 4);
+      const int64_t t = base + mm;
+      row16_route<J16>(lg + mm * ldE, bias_s, E, a.k, a.routed_scale, t < a.T, a.idx + t * a.k, a.w + t * a.k,
                        u.rsc[wave]);
     }
-    if (a.logits_out) {
+    if (a.logits_out && m.ncb == 1) {
       const int nrows = min(32, a.T - base);
-      for (int i = threadIdx.x; i < nrows * E; i += kPrefillThreads) {
-        const int m = i / E, e = i - m * E;
-        a.logits_out[(int64_t)(base + m) * E + e] = lg[m * ldE + e];
+      for (int i = threadIdx.x; i < nrows * E; i += kMmaThreads) {
+        const int mm = i / E, e = i - mm * E;
+        a.logits_out[(int64_t)(base + mm) * E + e] = lg[mm * ldE + e];
       }
     }
-  }
+  };
+  static_for<0, BM / 32>(pass);
+  if (m.ncb > 1) release_counter(&a.counters[rb]);
 }
 
 // ---------------------------------------------------------------------------
@@ -603,7 +758,10 @@ __global__ __launch_bounds__(kPrefillThreads) void gate_fused_kernel(TileArgs a)
 static GateTuning read_tuning() {
   GateTuning t;
   if (const char* v = getenv("NVR_SPLIT_MAX_T")) t.split_max_t = atoi(v);
-  if (const char* v = getenv("NVR_FUSED_BM")) t.fused_bm = atoi(v);
+  if (const char* v = getenv("NVR_MMA_BM")) t.mma_bm = atoi(v);
+  if (const char* v = getenv("NVR_MMA_NTW")) t.mma_ntw = atoi(v);
+  if (t.mma_bm != 32 && t.mma_bm != 64 && t.mma_bm != 128) t.mma_bm = 0;
+  if (t.mma_ntw < 1 || t.mma_ntw > 4 || (t.mma_bm / 32) * t.mma_ntw * 16 > 192) t.mma_ntw = 0;
   if (t.split_max_t < 0) t.split_max_t = 0;
   if (t.split_max_t > 16 * kMaxCounters) t.split_max_t = 16 * kMaxCounters;
   return t;
@@ -619,15 +777,7 @@ static int decode_slices(int64_t D) { return (int)((D / 16 + kDecSlice - 1) / kD
 GateKind gate_kind(int64_t T, int64_t D) {
   if (T <= kDecMaxT && decode_slices(D) <= kDecMaxSlices) return GateKind::kDecode;
   if (T <= gate_tuning().split_max_t) return GateKind::kTile;
-  return GateKind::kFused;
-}
-
-size_t gate_scratch_bytes(int64_t T, int64_t D, int64_t E) {
-  switch (gate_kind(T, D)) {
-    case GateKind::kDecode: return (size_t)decode_slices(D) * (size_t)T * (size_t)E * sizeof(float);
-    case GateKind::kTile: return (size_t)T * (size_t)E * sizeof(float);
-    default: return 0;
-  }
+  return GateKind::kMma;
 }
 
 template <bool QUANT>
@@ -655,33 +805,85 @@ static hipError_t launch_tile(const TileArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM, int NT, int J16>
-static hipError_t launch_fused_t(const TileArgs& a, hipStream_t stream) {
-  const int grid = (a.T + BM - 1) / BM;
-  const size_t lds = (size_t)32 * (a.E + 16) * sizeof(float);
-  gate_fused_kernel<BM, NT, J16><<<grid, kPrefillThreads, lds, stream>>>(a);
+// Prefill plan: BM tokens x 128 NTW experts per workgroup, NCB expert blocks
+// per token block. Among the layouts whose accumulators fit in registers,
+// prefer those that give every compute unit a workgroup, then the least
+// operand conversion per FLOP, (BM + 128 NTW) / (BM * 128 NTW): every
+// workgroup converts its BM x D token tile and its 128 NTW x D weight tile.
+struct MmaPlan {
+  int bm, ntw, ncb;
+};
+
+static MmaPlan plan_mma(int64_t T, int64_t E) {
+  const int tiles = (int)((E + 127) / 128);
+  const MmaPlan forced = {gate_tuning().mma_bm, gate_tuning().mma_ntw, 0};
+  if (forced.bm > 0 && forced.ntw > 0 && forced.ntw <= tiles) {
+    const int ncb = (tiles + forced.ntw - 1) / forced.ntw;
+    if (ncb == 1 || (T + forced.bm - 1) / forced.bm <= kMaxCounters) return {forced.bm, forced.ntw, ncb};
+  }
+  MmaPlan best = {32, tiles, 1};
+  double best_cost = 1e30;
+  int64_t best_wg = 0;
+  for (int ntw = 1; ntw <= tiles; ++ntw) {
+    if (tiles % ntw) continue;
+    const int ncb = tiles / ntw;
+    for (int bm : {128, 64, 32}) {
+      if ((bm / 32) * ntw * 16 > 192) continue;  // accumulator registers
+      const int64_t nrb = (T + bm - 1) / bm;
+      if (ncb > 1 && nrb > kMaxCounters) continue;
+      const int64_t wg = std::min<int64_t>(nrb * ncb, 256);
+      const double cost = (double)(bm + 128 * ntw) / ((double)bm * 128 * ntw);
+      if (wg > best_wg || (wg == best_wg && cost < best_cost)) {
+        best = {bm, ntw, ncb};
+        best_wg = wg;
+        best_cost = cost;
+      }
+    }
+  }
+  return best;
+}
+
+template <int BM, int NTW, int J16>
+static hipError_t launch_mma_t(const MmaArgs& m, hipStream_t stream) {
+  gate_mfma_kernel<BM, NTW, J16><<<m.nwg, kMmaThreads, 0, stream>>>(m);
   return hipGetLastError();
 }
 
-template <int BM>
-static hipError_t launch_fused_bm(const TileArgs& a, hipStream_t stream) {
-  const int nt = (a.E + 127) / 128;
-  if (nt <= 1) return a.E <= 64 ? launch_fused_t<BM, 1, 4>(a, stream) : launch_fused_t<BM, 1, 8>(a, stream);
-  if (nt <= 2) return launch_fused_t<BM, 2, 16>(a, stream);
-  if (nt <= 3) return launch_fused_t<BM, 3, 24>(a, stream);
-  return launch_fused_t<BM, 4, 32>(a, stream);
+template <int BM, int NTW>
+static hipError_t launch_mma_j(const MmaArgs& m, hipStream_t stream) {
+  const int E = m.t.E;
+  if (E <= 64) return launch_mma_t<BM, NTW, 4>(m, stream);
+  if (E <= 128) return launch_mma_t<BM, NTW, 8>(m, stream);
+  if (E <= 256) return launch_mma_t<BM, NTW, 16>(m, stream);
+  if (E <= 384) return launch_mma_t<BM, NTW, 24>(m, stream);
+  return launch_mma_t<BM, NTW, 32>(m, stream);
 }
 
-static hipError_t launch_fused(const TileArgs& a, hipStream_t stream) {
-  // Row tile: the largest of 128 / 64 / 32 that still gives every compute
-  // unit a workgroup (taller tiles reuse each converted weight for more rows).
-  // 128-row tiles only for E <= 256 (their accumulators, 16 x (E/32) fp32
-  // per lane, must stay in registers).
-  const int bm = gate_tuning().fused_bm > 0 ? gate_tuning().fused_bm
-                 : (a.T >= 128 * 256 && a.E <= 256 ? 128 : (a.T >= 64 * 256 ? 64 : 32));
-  if (bm >= 128) return launch_fused_bm<128>(a, stream);
-  if (bm >= 64) return launch_fused_bm<64>(a, stream);
-  return launch_fused_bm<32>(a, stream);
+static hipError_t launch_mma(const TileArgs& a, hipStream_t stream) {
+  const MmaPlan p = plan_mma(a.T, a.E);
+  MmaArgs m{a, p.ncb, 0, (int)((a.D + 128 * 4 - 1) / (128 * 4)) * 4};
+  m.nwg = (int)((a.T + p.bm - 1) / p.bm) * p.ncb;
+  switch (p.bm * 8 + p.ntw) {
+    case 128 * 8 + 1: return launch_mma_j<128, 1>(m, stream);
+    case 128 * 8 + 2: return launch_mma_j<128, 2>(m, stream);
+    case 128 * 8 + 3: return launch_mma_j<128, 3>(m, stream);
+    case 64 * 8 + 1: return launch_mma_j<64, 1>(m, stream);
+    case 64 * 8 + 2: return launch_mma_j<64, 2>(m, stream);
+    case 64 * 8 + 3: return launch_mma_j<64, 3>(m, stream);
+    case 64 * 8 + 4: return launch_mma_j<64, 4>(m, stream);
+    case 32 * 8 + 1: return launch_mma_j<32, 1>(m, stream);
+    case 32 * 8 + 2: return launch_mma_j<32, 2>(m, stream);
+    case 32 * 8 + 3: return launch_mma_j<32, 3>(m, stream);
+    default: return launch_mma_j<32, 4>(m, stream);
+  }
+}
+
+size_t gate_scratch_bytes(int64_t T, int64_t D, int64_t E) {
+  switch (gate_kind(T, D)) {
+    case GateKind::kDecode: return (size_t)decode_slices(D) * (size_t)T * (size_t)E * sizeof(float);
+    case GateKind::kTile: return (size_t)T * (size_t)E * sizeof(float);
+    default: return plan_mma(T, E).ncb > 1 ? (size_t)T * (size_t)E * sizeof(float) : 0;
+  }
 }
 
 hipError_t launch_gate(const uint8_t* xc, const uint8_t* xs, const float* gsa, const uint8_t* wc, const uint8_t* ws,
@@ -698,7 +900,7 @@ hipError_t launch_gate(const uint8_t* xc, const uint8_t* xs, const float* gsa, c
   }
   TileArgs a{xc, xs, gsa, wc, ws, gsw, bias, rs, (int)T, (int)D, (int)E, (int)k, idx, w, lo, lbuf, counters,
              (int)((D + 127) / 128)};
-  return kind == GateKind::kTile ? launch_tile(a, stream) : launch_fused(a, stream);
+  return kind == GateKind::kTile ? launch_tile(a, stream) : launch_mma(a, stream);
 }
 
 bool forward_single_launch(int64_t T, int64_t D) { return gate_kind(T, D) == GateKind::kDecode; }

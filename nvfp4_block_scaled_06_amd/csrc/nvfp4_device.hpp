@@ -514,17 +514,29 @@ __device__ __forceinline__ void wave_route_row(const float* Lrow, const float* b
 }
 
 // Throughput routing for many tokens: 16 lanes (one DPP row) per token, four
-// tokens per wavefront at once. Same six steps, same selection rule and the
-// same order as wave_route_row; the lower bound on the k-th key is the
-// smallest of the 16 lanes' maxima (16 groups >= k; for k > 16 no bound is
-// used). Lane l of a row holds experts l, l+16, ... (J16 of them). Each row
-// uses its own slice of `cand` (16 * J16 + 8 entries) and `sel` (32).
+// tokens per wavefront at once. Same six steps, selection rule and order as
+// wave_route_regs. Lane l of a row holds the J16 consecutive experts
+// l J16 .. l J16 + J16 - 1, read with 16-byte LDS loads (rows of logits and
+// the bias must be readable up to 16 J16 entries).
+//  1. keys as in wave_route_regs; lm = the lane's largest key;
+//  2. for k <= 16 the k-th largest of the 16 lane maxima is a lower bound on
+//     the k-th largest key (k distinct experts reach it). Each lane counts
+//     the lanes above it over 15 DPP row rotations; the bound is the smallest
+//     lane maximum with fewer than k lanes above it. Everything at or above
+//     it survives: usually k or a few more;
+//  3. for k > 16, or when more than 32 survive (flat or tied scores), the
+//     exact k-th largest key K is found bit by bit from the top (32 row
+//     counts of keys >= t); the survivors are then the keys above K plus the
+//     lowest-index experts whose key equals K, exactly k of them;
+//  4. the survivors (at most 32) are compacted by a row prefix sum and each
+//     is ranked against all of them with one batch of LDS reads; the weight
+//     sum is a DPP row sum and each chosen lane stores its output at its rank.
+constexpr int kRow16MaxSurvivors = 32;
+
 template <int J16>
 struct Row16Scratch {
-  uint64_t cand[4][16 * J16 + 8];
-  float sel_s[4][32];
-  int sel_i[4][32];
-  uint32_t count[4];
+  uint64_t cand[4][kRow16MaxSurvivors];
+  float cs[4][kRow16MaxSurvivors];
 };
 
 __device__ __forceinline__ uint32_t row_min_u32(uint32_t v) {
@@ -543,6 +555,14 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ int row_sum_i(int v) {
+  v += dpp_i<kDppXor1>(v);
+  v += dpp_i<kDppXor2>(v);
+  v += dpp_i<kDppHalfMirror>(v);
+  v += dpp_i<kDppMirror>(v);
+  return v;
+}
+
 // Inclusive prefix sum over the 16 lanes of each DPP row.
 __device__ __forceinline__ int row_scan(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
@@ -552,87 +572,152 @@ __device__ __forceinline__ int row_scan(int v) {
   return v;
 }
 
-// Routes token `row` (LDS logits Lrow, LDS bias) if `valid`; every lane of
-// the wavefront must call it (DPP), each 16-lane row with its own token.
+// Number of lanes of the row whose value exceeds this lane's (row_ror:R).
+template <int R>
+__device__ __forceinline__ int count_above(uint32_t v, int n) {
+  if constexpr (R < 16) return count_above<R + 1>(v, n + (dpp_u<0x120 + R>(v) > v ? 1 : 0));
+  return n;
+}
+
+// Survivors 0..NS-1 of a row (entries past the count are zero), ranked and
+// stored; NS = 16 or 32, lane l16 takes survivors l16 and l16 + 16.
+template <int J16, int NS>
+__device__ __forceinline__ void row16_rank_store(int C, int k, float routed_scale, bool valid, int l16, int rq,
+                                                 int32_t* __restrict__ out_idx, float* __restrict__ out_w,
+                                                 const Row16Scratch<J16>& sc) {
+  uint64_t all[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) all[u] = sc.cand[rq][u];
+  uint64_t mine[NS / 16];
+  float ms[NS / 16];
+  int rank[NS / 16];
+#pragma unroll
+  for (int h = 0; h < NS / 16; ++h) {
+    mine[h] = sc.cand[rq][l16 + 16 * h];
+    ms[h] = sc.cs[rq][l16 + 16 * h];
+    rank[h] = 0;
+  }
+#pragma unroll
+  for (int u = 0; u < NS; ++u)
+#pragma unroll
+    for (int h = 0; h < NS / 16; ++h) rank[h] += all[u] > mine[h] ? 1 : 0;
+  float part = 0.0f;
+  bool chosen[NS / 16];
+#pragma unroll
+  for (int h = 0; h < NS / 16; ++h) {
+    chosen[h] = l16 + 16 * h < C && rank[h] < k;
+    part += chosen[h] ? ms[h] : 0.0f;
+  }
+  const float f = routed_scale * __builtin_amdgcn_rcpf(row_sum(part));
+  if (valid) {
+#pragma unroll
+    for (int h = 0; h < NS / 16; ++h)
+      if (chosen[h]) {
+        out_idx[rank[h]] = (int)(0xFFFFFFFFu - (uint32_t)mine[h]);
+        out_w[rank[h]] = ms[h] * f;
+      }
+  }
+}
+
 template <int J16>
 __device__ __forceinline__ void row16_route(const float* Lrow, const float* bias_lds, int E, int k,
                                             float routed_scale, bool valid, int32_t* __restrict__ out_idx,
                                             float* __restrict__ out_w, Row16Scratch<J16>& sc) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, rq = lane >> 4;
+  const int e0 = l16 * J16;
   uint32_t key[J16];
   float s[J16];
   uint32_t lm = 0u;
 #pragma unroll
-  for (int j = 0; j < J16; ++j) {
-    const int e = l16 + 16 * j;
-    const int ec = min(e, E - 1);
-    s[j] = sigmoid_fast(Lrow[ec]);
-    key[j] = (e < E && valid) ? score_key(s[j] + bias_lds[ec]) : 0u;
-    lm = max(lm, key[j]);
-  }
-  const uint32_t tau = k <= 16 ? row_min_u32(lm) : 1u;
-  int cnt = 0;
+  for (int j4 = 0; j4 < J16 / 4; ++j4) {
+    const float4 L4 = *reinterpret_cast<const float4*>(Lrow + e0 + 4 * j4);
+    const float4 B4 = *reinterpret_cast<const float4*>(bias_lds + e0 + 4 * j4);
+    const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Bv[4] = {B4.x, B4.y, B4.z, B4.w};
 #pragma unroll
-  for (int j = 0; j < J16; ++j) cnt += (key[j] != 0u && key[j] >= tau) ? 1 : 0;
-  const int incl = row_scan(cnt);
-  int pos = incl - cnt;
-#pragma unroll
-  for (int j = 0; j < J16; ++j) {
-    if (key[j] != 0u && key[j] >= tau) {
-      sc.cand[rq][pos] = ((uint64_t)key[j] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(l16 + 16 * j));
-      ++pos;
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * j4 + i;
+      s[j] = sigmoid_fast(Lv[i]);
+      key[j] = (e0 + j < E && valid) ? score_key(s[j] + Bv[i]) : 0u;
+      lm = max(lm, key[j]);
     }
   }
-  if (l16 == 15) sc.count[rq] = (uint32_t)incl;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int C = (int)sc.count[rq];
-  if (l16 < 8) sc.cand[rq][C + l16] = 0ull;  // padding: ranks below nobody
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // Rank of each survivor; the loop bound is the wavefront's largest count.
+  // Survivor rule: a nonzero key > hi, or == hi among this lane's first
+  // `ties` such keys (the bound: hi = tau - 1, no ties taken; the exact
+  // search: hi = K, ties shared out in index order).
+  uint32_t hi = 0u;
+  int ties = 0x7FFFFFFF;
+  int C = kRow16MaxSurvivors + 1;
+  if (k <= 16) {
+    const int above = count_above<1>(lm, 0);
+    const uint32_t tau = row_min_u32(above < k ? lm : 0xFFFFFFFFu);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < J16; ++j) cnt += (key[j] != 0u && key[j] >= tau) ? 1 : 0;
+    C = row_sum_i(cnt);
+    hi = tau > 0u ? tau - 1u : 0u;  // key > hi <=> key >= tau, for the nonzero keys
+    ties = 0;
+  }
   int cmax = C;
   cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 0));
   cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 16));
   cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 32));
   cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 48));
-  for (int c = l16; c < ((cmax + 15) & ~15); c += 16) {
-    const int cc = min(c, max(C - 1, 0));
-    const uint64_t mine = sc.cand[rq][cc];
-    int rank = 0;
-    for (int c0 = 0; c0 < cmax; c0 += 8) {
-      uint64_t v[8];
+  if (cmax > kRow16MaxSurvivors) {
+    // Exact k-th largest key K of each row, bit by bit: the largest t with at
+    // least k keys >= t.
+    uint32_t K = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t t = K | (1u << bit);
+      int cnt = 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = sc.cand[rq][min(c0 + u, C + 7)];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) rank += (c0 + u < C && v[u] > mine) ? 1 : 0;
+      for (int j = 0; j < J16; ++j) cnt += key[j] >= t ? 1 : 0;
+      if (row_sum_i(cnt) >= k) K = t;
     }
-    if (c < C && rank < k) {
-      const int e = (int)(0xFFFFFFFFu - (uint32_t)mine);
-      sc.sel_i[rq][rank] = e;
-      sc.sel_s[rq][rank] = sigmoid_fast(Lrow[e]);  // the same s the key was formed from
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < J16; ++j) {
+      gt += key[j] > K ? 1 : 0;
+      eq += (key[j] == K && key[j] != 0u) ? 1 : 0;
+    }
+    hi = K;
+    ties = k - row_sum_i(gt);                 // equal keys still to take, lowest index first
+    const int eq_before = row_scan(eq) - eq;  // equal keys in lanes before this one
+    ties -= eq_before;                        // this lane may take its first `ties` equal keys
+    C = k;
+  }
+  // Compact the survivors (at most 32 per row).
+  int cnt = 0, teq = 0;
+  bool surv[J16];
+#pragma unroll
+  for (int j = 0; j < J16; ++j) {
+    const bool eq = key[j] == hi && key[j] != 0u;
+    surv[j] = key[j] != 0u && (key[j] > hi || (eq && teq < ties));
+    teq += eq ? 1 : 0;
+    cnt += surv[j] ? 1 : 0;
+  }
+  int pos = row_scan(cnt) - cnt;
+#pragma unroll
+  for (int j = 0; j < J16; ++j) {
+    if (surv[j]) {
+      sc.cand[rq][pos] = ((uint64_t)key[j] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(e0 + j));
+      sc.cs[rq][pos] = s[j];
+      ++pos;
     }
   }
+  C = row_sum_i(cnt);
+  cmax = C;
+  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 0));
+  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 16));
+  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 32));
+  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 48));
+  const int ns = cmax <= 16 ? 16 : 32;
+  if (C <= l16) sc.cand[rq][l16] = 0ull;  // entries past the count rank below everything
+  if (ns == 32 && C <= l16 + 16) sc.cand[rq][l16 + 16] = 0ull;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // k <= 32: lanes l16 and l16 + 16 cover the chosen list.
-  const float s0 = l16 < k ? sc.sel_s[rq][l16] : 0.0f;
-  const float s1 = l16 + 16 < k ? sc.sel_s[rq][l16 + 16] : 0.0f;
-  const float ssum = row_sum(s0 + s1);
-  const float f = routed_scale * __builtin_amdgcn_rcpf(ssum);
-  if (valid) {
-    if (l16 < k) {
-      out_idx[l16] = sc.sel_i[rq][l16];
-      out_w[l16] = s0 * f;
-    }
-    if (l16 + 16 < k) {
-      out_idx[l16 + 16] = sc.sel_i[rq][l16 + 16];
-      out_w[l16 + 16] = s1 * f;
-    }
-  }
+  if (ns == 16) row16_rank_store<J16, 16>(C, k, routed_scale, valid, l16, rq, out_idx, out_w, sc);
+  else row16_rank_store<J16, 32>(C, k, routed_scale, valid, l16, rq, out_idx, out_w, sc);
 }
 
 }  // namespace nvr

@@ -22,8 +22,10 @@ bool shape_ok(int64_t rows, int64_t D) {
 int status_from(hipError_t e) { return e == hipSuccess ? ROUTER_OK : ROUTER_EHIP; }
 
 size_t gate_need(int64_t T, int64_t D, int64_t E) {
-  if (T == 0 || nvr::gate_kind(T, D) == nvr::GateKind::kFused) return 0;
-  return nvr::kScratchOffset + nvr::gate_scratch_bytes(T, D, E);
+  if (T == 0) return 0;
+  const size_t scratch = nvr::gate_scratch_bytes(T, D, E);
+  if (nvr::gate_kind(T, D) == nvr::GateKind::kMma && scratch == 0) return 0;  // no counters, no scratch
+  return nvr::kScratchOffset + scratch;
 }
 
 size_t quantize_need(int64_t rows, int64_t D, bool override_given) {

@@ -16,7 +16,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 //   [kScratchOffset, ...)  per-call scratch (partial maxima of the quantizer,
 //                          the slice partials of the decode gate, the [T, E]
 //                          logits of the tile gate).
-constexpr size_t kCounterBytes = 256;
+constexpr size_t kCounterBytes = 4096;
 constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(uint32_t));
 constexpr size_t kScratchOffset = kCounterBytes;
 
@@ -25,16 +25,19 @@ constexpr int kAmaxPartials = 1024;       // workgroups of the amax pass
 constexpr int kQuantMaxGrid = 8192;  // workgroups of the quantize pass
 
 // Gate dispatch by token count: decode (T <= 4 and D <= 16384: one workgroup
-// per 16 experts and 1024-element K slice, the last workgroup routes), tile (T <= split_max_t: 16x16 MFMA tiles, the last
-// workgroup of each 16-row tile routes), fused (larger T: one workgroup per
-// 32 rows and all experts, routing in the same workgroup).
+// per 16 experts and 1024-element K slice, the last workgroup routes), tile
+// (T <= split_max_t: 16x16 MFMA tiles, the last workgroup of each 16-row tile
+// routes), mfma (larger T: BM tokens x 128 NTW experts per workgroup on
+// 32x32 MFMA; routed in the workgroup, or by the last expert block of each
+// token block when E is split).
 struct GateTuning {
   int split_max_t = 256;
-  int fused_bm = 0;  // 0: by T; else 32 / 64 / 128 rows per workgroup
+  int mma_bm = 0;   // prefill tokens per workgroup (32 / 64 / 128); 0 = planned
+  int mma_ntw = 0;  // prefill 32-expert tiles per wavefront; 0 = planned
 };
 const GateTuning& gate_tuning();
 
-enum class GateKind { kDecode, kTile, kFused };
+enum class GateKind { kDecode, kTile, kMma };
 GateKind gate_kind(int64_t T, int64_t D);
 
 size_t quantize_scratch_bytes();

@@ -47,10 +47,11 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     n = lib.router_workspace_bytes(1, 7168, 256, 8)
-    assert n >= 256 + 4096 and n % 4 == 0
+    assert n >= 4096 + 4096 and n % 4 == 0
     assert lib.router_workspace_bytes(64, 7168, 256, 8) >= lib.router_workspace_bytes(1, 7168, 256, 8)
-    assert lib.router_workspace_bytes(8192, 7168, 256, 8) == 256 + 4096  # fused gate needs no scratch
-    assert lib.router_workspace_bytes(1, 7168, 256, 8) == 256 + 7 * 256 * 4  # decode: 7 K slices of partials
+    assert lib.router_workspace_bytes(8192, 7168, 256, 8) == 4096 + 8192 * 256 * 4  # split experts: [T, E] logits
+    assert lib.router_workspace_bytes(32768, 7168, 384, 8) == 4096 + 4096  # all experts per workgroup: quantizer only
+    assert lib.router_workspace_bytes(1, 7168, 256, 8) == 4096 + 7 * 256 * 4  # decode: 7 K slices of partials
     for bad in [(1, 7168, 256, 0), (1, 7168, 256, 257), (1, 7169, 256, 8), (-1, 7168, 256, 8), (1, 7168, 0, 1),
                 (1, 7168, 513, 8)]:
         assert lib.router_workspace_bytes(*bad) == 0, bad

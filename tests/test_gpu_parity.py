@@ -247,10 +247,14 @@ def synth(shape, seed, scale=1.0):
     (3, 1024, 512, 32),    # largest E and k
     (17, 768, 256, 8),     # ragged 16-row tiles
     (256, 1024, 256, 8),   # largest split-gate T
-    (257, 1024, 256, 8),   # smallest fused-gate T, ragged 32-row tile
-    (300, 2048, 384, 8),   # fused, 3 expert tiles per wave
-    (65, 4096, 100, 6),    # fused-size E not a multiple of 32 (split path at this T)
+    (257, 1024, 256, 8),   # smallest MFMA-gate T, ragged row tile
+    (300, 2048, 384, 8),   # MFMA gate, 3 expert tiles per wave
+    (65, 4096, 100, 6),    # E not a multiple of 32 (tile gate at this T)
     (96, 8192, 64, 4),
+    (600, 1056, 100, 6),   # MFMA gate: D not a multiple of 128, E not a multiple of 32
+    (640, 384, 200, 8),    # MFMA gate, experts split over workgroups, second block partly empty
+    (512, 512, 512, 32),   # MFMA gate, largest E and k
+    (8200, 256, 256, 8),   # split experts, ragged last token block
 ])
 def test_gate_shapes(dev, ws, T, D, E, k):
     log(f"gate shape T={T} D={D} E={E} k={k}")
