@@ -460,7 +460,7 @@ struct MmaArgs {
   TileArgs t;
   int ncb;     // expert blocks (workgroups per token block)
   int nwg;     // workgroups
-  int nsteps;  // 128-element K steps, rounded up to a multiple of 4 (every ring depth divides it)
+  int nsteps;  // 128-element K steps, rounded up to a multiple of 8 (K groups times any ring depth)
 };
 
 // Token rows per thread in the A tile (4 threads per row): one slot per 64
@@ -495,7 +495,7 @@ struct MmaPtrs {
 template <int BM, int NTW>
 __device__ __forceinline__ MmaPtrs<BM, NTW> mma_ptrs(const TileArgs& a, int row0, int col0, int wave, int lane) {
   MmaPtrs<BM, NTW> P;
-  const int tid = threadIdx.x, q = tid & 3, r = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x & (kMmaThreads - 1), q = tid & 3, r = lane & 31, h = lane >> 5;
   const int64_t rowc = a.D / 2, rows = a.D / 16;
   P.ka = 32 * q;
   P.kb = 32 * h;
@@ -546,7 +546,7 @@ __device__ __forceinline__ void mma_load(MmaRegs<BM, NTW>& R, const MmaPtrs<BM, 
 // This thread's A chunks, converted, into the LDS tile.
 template <int BM, int NTW>
 __device__ __forceinline__ void mma_store_a(const MmaRegs<BM, NTW>& R, _Float16* abuf) {
-  const int tid = threadIdx.x, q = tid & 3;
+  const int tid = threadIdx.x & (kMmaThreads - 1), q = tid & 3;
 #pragma unroll
   for (int i = 0; i < mma_row_slots<BM>(); ++i) {
     const int r = (tid >> 2) + 64 * i;
@@ -603,26 +603,32 @@ __device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& R, const _Float
   }
 }
 
-template <int BM, int NTW, int J16>
+template <int BM, int NTW, int J16, int KS>
 union MmaLds {
-  _Float16 abuf[2][BM * kMmaARow];  // K loop: the converted A tiles
-  Row16Scratch<J16> rsc[4];         // epilogue: one router scratch per wavefront
+  _Float16 abuf[KS][2][BM * kMmaARow];  // K loop: each K group's converted A tiles, double-buffered
+  struct {
+    float lg[32 * (16 * J16 + 4)];      // epilogue: 32 tokens' logits at a time
+    Row16Scratch<J16> rsc[4 * KS];      // one router scratch per wavefront
+  } epi;
 };
 
-// One wavefront per SIMD is the common residency (the LDS tile allows one or
-// two workgroups per compute unit), so the kernel may use the whole register
-// file rather than spill.
-template <int BM, int NTW, int J16>
-__global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gate_mfma_kernel(MmaArgs m) {
+// KS K groups of four wavefronts: group g takes K steps g, g + KS, ... and
+// both groups hold the same output tiles (wavefront w and w + 4 on one
+// SIMD), so one group's conversion work overlaps the other's MFMAs; their
+// accumulators are added in the epilogue. One wavefront per SIMD otherwise
+// (KS = 1), the register file then allowing the widest tiles.
+template <int BM, int NTW, int J16, int KS>
+__global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_eu(KS, KS))) void gate_mfma_kernel(
+    MmaArgs m) {
   constexpr int ldE = 16 * J16 + 4;  // the router reads 16 J16 entries per row, 16 bytes at a time
-  static_assert(sizeof(MmaLds<BM, NTW, J16>) + (512 + 32 * ldE) * sizeof(float) + 16 <= 160 * 1024,
+  static_assert(sizeof(MmaLds<BM, NTW, J16, KS>) + 512 * sizeof(float) + 16 <= 160 * 1024,
                 "LDS of one workgroup must fit a compute unit");
   const TileArgs& a = m.t;
-  __shared__ __attribute__((aligned(16))) MmaLds<BM, NTW, J16> u;
+  __shared__ __attribute__((aligned(16))) MmaLds<BM, NTW, J16, KS> u;
   __shared__ __attribute__((aligned(16))) float bias_s[512];
-  __shared__ __attribute__((aligned(16))) float lg[32 * ldE];  // 32 tokens' logits at a time
   __shared__ uint32_t s_last;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* lg = u.epi.lg;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wt = wave & 3, grp = wave >> 2;
   const int E = a.E;
   // Token block / expert block of this workgroup (XCD-grouped numbering).
   const int nq = m.nwg >> 3, nr = m.nwg & 7, bx = blockIdx.x & 7;
@@ -631,7 +637,7 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(1, 
   const int row0 = rb * BM, col0 = cb * 128 * NTW;
   const int nsteps = m.nsteps;
   const float bias0 = (int)threadIdx.x < E ? a.bias[threadIdx.x] : 0.0f;
-  const float bias1 = (int)threadIdx.x + 256 < E ? a.bias[threadIdx.x + 256] : 0.0f;
+  const float bias1 = KS == 1 && (int)threadIdx.x + 256 < E ? a.bias[threadIdx.x + 256] : 0.0f;
   const float gsa = load_early(a.gsa), gsw = load_early(a.gsw);
 
   constexpr int NS = mma_sets<BM, NTW>();
@@ -645,21 +651,21 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[q][rt][t][v] = 0.0f;
 
-  // Steps are padded to a multiple of the ring depth: padding steps load
-  // nothing (k >= D) and add zeros.
-  const MmaPtrs<BM, NTW> P = mma_ptrs<BM, NTW>(a, row0, col0, wave, lane);
+  // Steps are padded to a multiple of KS times the ring depth: padding steps
+  // load nothing (k >= D) and add zeros.
+  const MmaPtrs<BM, NTW> P = mma_ptrs<BM, NTW>(a, row0, col0, wt, lane);
   constexpr int RING = mma_ring<BM, NTW>();
   MmaRegs<BM, NTW> R[RING];
 #pragma unroll
-  for (int p = 0; p < RING; ++p) mma_load<BM, NTW>(R[p], P, a.D, p);
-  mma_store_a<BM, NTW>(R[0], u.abuf[0]);
+  for (int p = 0; p < RING; ++p) mma_load<BM, NTW>(R[p], P, a.D, KS * p + grp);
+  mma_store_a<BM, NTW>(R[0], u.abuf[grp][0]);
   __syncthreads();
-  for (int s0 = 0; s0 < nsteps; s0 += RING) {
+  for (int s0 = 0; s0 < nsteps; s0 += KS * RING) {
 #pragma unroll
     for (int p = 0; p < RING; ++p) {
-      mma_step<BM, NTW>(R[p], u.abuf[p & 1], lane, acc);
-      mma_store_a<BM, NTW>(R[(p + 1) % RING], u.abuf[(p + 1) & 1]);
-      mma_load<BM, NTW>(R[p], P, a.D, s0 + p + RING);
+      mma_step<BM, NTW>(R[p], u.abuf[grp][p & 1], lane, acc);
+      mma_store_a<BM, NTW>(R[(p + 1) % RING], u.abuf[grp][(p + 1) & 1]);
+      mma_load<BM, NTW>(R[p], P, a.D, s0 + KS * (p + RING) + grp);
       __syncthreads();
     }
   }
@@ -671,28 +677,60 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(1, 
   }
 
   // Epilogue. 32x32 accumulator layout: value v of lane (r, h) is row
-  // 8(v/4) + 4h + v%4, column r of its tile.
+  // 8(v/4) + 4h + v%4, column r of its tile. With two K groups, group 1
+  // leaves its sums in LDS and group 0 adds them (a fixed order).
   const float scale = gsa * gsw;
   const int r = lane & 31, h = lane >> 5;
   if ((int)threadIdx.x < E) bias_s[threadIdx.x] = bias0;
-  if ((int)threadIdx.x + 256 < E) bias_s[threadIdx.x + 256] = bias1;
-  if (m.ncb > 1) {
-    // Split experts: store this block's logits, then the last block routes.
-#pragma unroll
-    for (int rt = 0; rt < BM / 32; ++rt)
+  if (KS == 1 && (int)threadIdx.x + 256 < E) bias_s[threadIdx.x + 256] = bias1;
+  // Pass rt: this K group's scaled sums of row tile rt into lg (group 1 first,
+  // then group 0 adds), columns local to the workgroup's expert block when
+  // `local`, else the expert index.
+  auto tile_to_lds = [&](auto rtc, bool local) {
+    constexpr int rt = decltype(rtc)::value;
+    if (KS == 2 && grp == 1) {
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
-        const int e = col0 + (wave + 4 * t) * 32 + r;
+        const int c = (wt + 4 * t) * 32 + r;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) lg[(8 * (v >> 2) + 4 * h + (v & 3)) * ldE + c] = acc[0][rt][t][v];
+      }
+    }
+    if (KS == 2) __syncthreads();
+    if (grp == 0) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const int c = (wt + 4 * t) * 32 + r;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int64_t row = row0 + rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (e < E && row < a.T) {
-            const float L = acc[0][rt][t][v] * scale;
-            store_coherent(a.lbuf + row * E + e, L);
-            if (a.logits_out) a.logits_out[row * E + e] = L;
-          }
+          float* d = &lg[(8 * (v >> 2) + 4 * h + (v & 3)) * ldE + c];
+          *d = (KS == 2 ? acc[0][rt][t][v] + *d : acc[0][rt][t][v]) * scale;
         }
       }
+    }
+    (void)local;
+  };
+  if (m.ncb > 1) {
+    // Split experts: this block's logits to the workspace, then the last
+    // block of the token block routes it.
+    auto store_pass = [&](auto rtc) {
+      constexpr int rt = decltype(rtc)::value;
+      const int base = row0 + rt * 32;
+      if (base >= a.T) return;  // uniform
+      __syncthreads();
+      tile_to_lds(rtc, true);
+      __syncthreads();
+      const int nrows = min(32, a.T - base);
+      for (int i = threadIdx.x; i < 32 * 128 * NTW; i += kMmaThreads * KS) {
+        const int mm = i / (128 * NTW), c = i - mm * (128 * NTW), e = col0 + c;
+        if (mm < nrows && e < E) {
+          const float L = lg[mm * ldE + c];
+          store_coherent(a.lbuf + (int64_t)(base + mm) * E + e, L);
+          if (a.logits_out) a.logits_out[(int64_t)(base + mm) * E + e] = L;
+        }
+      }
+    };
+    static_for<0, BM / 32>(store_pass);
     if (!arrive_last(&a.counters[rb], m.ncb, &s_last)) return;
   }
   // Passes of 32 tokens; a compile-time row tile index keeps the accumulator
@@ -703,46 +741,41 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(1, 
     if (base >= a.T) return;  // uniform
     __syncthreads();
     if (m.ncb > 1) {
-      // Wavefront w gathers rows w, w + 4, ...; lane l columns l, l + 64, ...
-      // All of its loads are issued before the first store.
+      // Gather the token block's logits from every expert block: wavefront w
+      // takes rows w, w + 4KS, ...; lane l columns l, l + 64, ...; all loads
+      // are issued before the first store.
       const int nrows = min(32, a.T - base);
-      float v[8][J16 / 4];
+      constexpr int RR = 32 / (4 * KS);
+      float v[RR][J16 / 4];
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr)
+      for (int rr = 0; rr < RR; ++rr)
 #pragma unroll
         for (int cc = 0; cc < J16 / 4; ++cc) {
-          const int mm = wave + 4 * rr, e = lane + 64 * cc;
+          const int mm = wave + 4 * KS * rr, e = lane + 64 * cc;
           v[rr][cc] = (mm < nrows && e < E) ? load_coherent(a.lbuf + (int64_t)(base + mm) * E + e) : 0.0f;
         }
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr)
+      for (int rr = 0; rr < RR; ++rr)
 #pragma unroll
         for (int cc = 0; cc < J16 / 4; ++cc) {
-          const int mm = wave + 4 * rr, e = lane + 64 * cc;
+          const int mm = wave + 4 * KS * rr, e = lane + 64 * cc;
           if (mm < nrows && e < E) lg[mm * ldE + e] = v[rr][cc];
         }
     } else {
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        const int e = (wave + 4 * t) * 32 + r;
-        if (e < E) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) lg[(8 * (v >> 2) + 4 * h + (v & 3)) * ldE + e] = acc[0][rt][t][v] * scale;
-        }
-      }
+      tile_to_lds(rtc, false);
     }
     __syncthreads();
-    // 32 rows: wavefront w routes rows 8w .. 8w+7, four at a time.
+    // 32 rows: wavefront w routes rows (32 / 4KS) w .. , four at a time.
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int mm = wave * 8 + half * 4 + (lane >> 4);
+    for (int q = 0; q < 2 / KS; ++q) {
+      const int mm = wave * (8 / KS) + q * 4 + (lane >> 4);
       const int64_t t = base + mm;
       row16_route<J16>(lg + mm * ldE, bias_s, E, a.k, a.routed_scale, t < a.T, a.idx + t * a.k, a.w + t * a.k,
-                       u.rsc[wave]);
+                       u.epi.rsc[wave]);
     }
     if (a.logits_out && m.ncb == 1) {
       const int nrows = min(32, a.T - base);
-      for (int i = threadIdx.x; i < nrows * E; i += kMmaThreads) {
+      for (int i = threadIdx.x; i < nrows * E; i += kMmaThreads * KS) {
         const int mm = i / E, e = i - mm * E;
         a.logits_out[(int64_t)(base + mm) * E + e] = lg[mm * ldE + e];
       }
@@ -843,9 +876,17 @@ static MmaPlan plan_mma(int64_t T, int64_t E) {
   return best;
 }
 
+// Two K groups (eight wavefronts) when a wavefront's accumulators leave room
+// for two wavefronts per SIMD.
+template <int BM, int NTW>
+constexpr int mma_ksplit() {
+  return (BM / 32) * NTW <= 2 ? 2 : 1;
+}
+
 template <int BM, int NTW, int J16>
 static hipError_t launch_mma_t(const MmaArgs& m, hipStream_t stream) {
-  gate_mfma_kernel<BM, NTW, J16><<<m.nwg, kMmaThreads, 0, stream>>>(m);
+  constexpr int KS = mma_ksplit<BM, NTW>();
+  gate_mfma_kernel<BM, NTW, J16, KS><<<m.nwg, kMmaThreads * KS, 0, stream>>>(m);
   return hipGetLastError();
 }
 
@@ -861,7 +902,7 @@ static hipError_t launch_mma_j(const MmaArgs& m, hipStream_t stream) {
 
 static hipError_t launch_mma(const TileArgs& a, hipStream_t stream) {
   const MmaPlan p = plan_mma(a.T, a.E);
-  MmaArgs m{a, p.ncb, 0, (int)((a.D + 128 * 4 - 1) / (128 * 4)) * 4};
+  MmaArgs m{a, p.ncb, 0, (int)((a.D + 128 * 8 - 1) / (128 * 8)) * 8};
   m.nwg = (int)((a.T + p.bm - 1) / p.bm) * p.ncb;
   switch (p.bm * 8 + p.ntw) {
     case 128 * 8 + 1: return launch_mma_j<128, 1>(m, stream);
