@@ -478,17 +478,24 @@ struct MmaRegs {
   uint32_t bs[NTW][2];
 };
 
-// Per-thread operand addresses, formed once; a step adds 64 code bytes and
-// 8 scale bytes. A chunk is loaded only if it lies inside the row (k < D)
-// and the row exists; otherwise it stays zero and adds nothing.
+// Operand reads are raw buffer loads: each workgroup's descriptors cover
+// only its token rows and its expert rows, and a read past a descriptor's
+// end returns zeros. Rows past T or E and chunks past D (given an
+// out-of-range offset) therefore load zeros without a branch, so the wait
+// counters of the load ring stay exact. Offsets are per lane; a step adds 64
+// code bytes and 8 scale bytes.
+constexpr uint32_t kMmaOob = 0x80000000u;  // beyond every descriptor's range
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
 template <int BM, int NTW>
 struct MmaPtrs {
-  const uint8_t* a[mma_row_slots<BM>()];
-  const uint8_t* as[mma_row_slots<BM>()];
-  bool aok[mma_row_slots<BM>()];
-  const uint8_t* b[NTW];
-  const uint8_t* bs[NTW];
-  bool bok[NTW];
+  __amdgpu_buffer_rsrc_t xc, xs, wc, ws;
+  uint32_t a[mma_row_slots<BM>()], as[mma_row_slots<BM>()];
+  uint32_t b[NTW], bs[NTW];
   int ka, kb;  // K offset of this thread's A chunk / this lane's first B chunk within a step
 };
 
@@ -497,23 +504,24 @@ __device__ __forceinline__ MmaPtrs<BM, NTW> mma_ptrs(const TileArgs& a, int row0
   MmaPtrs<BM, NTW> P;
   const int tid = threadIdx.x & (kMmaThreads - 1), q = tid & 3, r = lane & 31, h = lane >> 5;
   const int64_t rowc = a.D / 2, rows = a.D / 16;
+  const int64_t nr = min((int64_t)BM, (int64_t)a.T - row0), nc = min((int64_t)128 * NTW, (int64_t)a.E - col0);
+  P.xc = make_rsrc(a.xc + row0 * rowc, nr * rowc);
+  P.xs = make_rsrc(a.xs + row0 * rows, nr * rows);
+  P.wc = make_rsrc(a.wc + col0 * rowc, nc * rowc);
+  P.ws = make_rsrc(a.ws + col0 * rows, nc * rows);
   P.ka = 32 * q;
   P.kb = 32 * h;
 #pragma unroll
   for (int i = 0; i < mma_row_slots<BM>(); ++i) {
-    const int64_t row = row0 + (tid >> 2) + 64 * i;
-    P.aok[i] = (tid >> 2) + 64 * i < BM && row < a.T;
-    const int64_t rr = P.aok[i] ? row : 0;
-    P.a[i] = a.xc + rr * rowc + 16 * q;
-    P.as[i] = a.xs + rr * rows + 2 * q;
+    const int rl = (tid >> 2) + 64 * i;  // row within the tile
+    P.a[i] = rl < BM ? (uint32_t)(rl * rowc + 16 * q) : kMmaOob;
+    P.as[i] = rl < BM ? (uint32_t)(rl * rows + 2 * q) : kMmaOob;
   }
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
-    const int64_t e = col0 + (wave + 4 * t) * 32 + r;
-    P.bok[t] = e < a.E;
-    const int64_t ee = P.bok[t] ? e : 0;
-    P.b[t] = a.wc + ee * rowc + 16 * h;
-    P.bs[t] = a.ws + ee * rows + 2 * h;
+    const int el = (wave + 4 * t) * 32 + r;  // expert within the block
+    P.b[t] = (uint32_t)(el * rowc + 16 * h);
+    P.bs[t] = (uint32_t)(el * rows + 2 * h);
   }
   return P;
 }
@@ -521,26 +529,24 @@ __device__ __forceinline__ MmaPtrs<BM, NTW> mma_ptrs(const TileArgs& a, int row0
 template <int BM, int NTW>
 __device__ __forceinline__ void mma_load(MmaRegs<BM, NTW>& R, const MmaPtrs<BM, NTW>& P, int D, int step) {
   const int k0 = step * 128;
+  const bool aok = k0 + P.ka < D;
 #pragma unroll
   for (int i = 0; i < mma_row_slots<BM>(); ++i) {
-    R.a[i] = u32x4_t{0u, 0u, 0u, 0u};
-    R.as[i] = 0u;
-    if (P.aok[i] && k0 + P.ka < D) {
-      R.a[i] = *reinterpret_cast<const u32x4_t*>(P.a[i] + 64 * step);
-      R.as[i] = *reinterpret_cast<const uint16_t*>(P.as[i] + 8 * step);
-    }
+    const uint32_t oc = aok ? P.a[i] + 64 * step : kMmaOob, os = aok ? P.as[i] + 8 * step : kMmaOob;
+    R.a[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(P.xc, oc, 0, 0));
+    R.as[i] = __builtin_amdgcn_raw_buffer_load_b16(P.xs, os, 0, 0);
   }
 #pragma unroll
-  for (int t = 0; t < NTW; ++t)
+  for (int c = 0; c < 2; ++c) {
+    const bool bok = k0 + 64 * c + P.kb < D;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      R.b[t][c] = u32x4_t{0u, 0u, 0u, 0u};
-      R.bs[t][c] = 0u;
-      if (P.bok[t] && k0 + 64 * c + P.kb < D) {
-        R.b[t][c] = *reinterpret_cast<const u32x4_t*>(P.b[t] + 64 * step + 32 * c);
-        R.bs[t][c] = *reinterpret_cast<const uint16_t*>(P.bs[t] + 8 * step + 4 * c);
-      }
+    for (int t = 0; t < NTW; ++t) {
+      const uint32_t oc = bok ? P.b[t] + 64 * step + 32 * c : kMmaOob;
+      const uint32_t os = bok ? P.bs[t] + 8 * step + 4 * c : kMmaOob;
+      R.b[t][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(P.wc, oc, 0, 0));
+      R.bs[t][c] = __builtin_amdgcn_raw_buffer_load_b16(P.ws, os, 0, 0);
     }
+  }
 }
 
 // This thread's A chunks, converted, into the LDS tile.
@@ -568,13 +574,9 @@ constexpr int mma_sets() {
   return (BM / 32) * NTW < 4 ? 2 : 1;
 }
 
-// One step's MFMAs: B converted from registers, A read from the LDS tile.
+// B fragments of one step, converted from this lane's raw chunks.
 template <int BM, int NTW>
-__device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& R, const _Float16* abuf, int lane,
-                                         f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
-  constexpr int NS = mma_sets<BM, NTW>();
-  const int r = lane & 31, h = lane >> 5;
-  half8_t B[NTW][8];
+__device__ __forceinline__ void mma_convert_b(const MmaRegs<BM, NTW>& R, half8_t (&B)[NTW][8]) {
 #pragma unroll
   for (int t = 0; t < NTW; ++t)
 #pragma unroll
@@ -585,8 +587,21 @@ __device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& R, const _Float
       B[t][4 * c + 2] = fp4x8_to_f16(R.b[t][c][2], s1);
       B[t][4 * c + 3] = fp4x8_to_f16(R.b[t][c][3], s1);
     }
-  // A fragments one 32-row tile at a time (eight ds_read_b128 issued
-  // together), each used against every expert tile of the wavefront.
+}
+
+// One pipelined step: the MFMAs of step s (A from the LDS tile, B converted
+// the step before) with the conversion work of step s + 1 — its B fragments
+// into Bn and its A chunks into the other LDS tile — interleaved between
+// them (scheduling groups: one MFMA, then a few VALU instructions), so that
+// a single wavefront keeps both the matrix core and the VALU busy.
+template <int BM, int NTW>
+__device__ __forceinline__ void mma_step(const half8_t (&B)[NTW][8], const _Float16* abuf, const MmaRegs<BM, NTW>& Rn,
+                                         half8_t (&Bn)[NTW][8], _Float16* abuf_n, int lane,
+                                         f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
+  constexpr int NS = mma_sets<BM, NTW>();
+  const int r = lane & 31, h = lane >> 5;
+  // A fragments one 32-row tile at a time, each used against every expert
+  // tile; a tile's eight LDS reads are issued together.
 #pragma unroll
   for (int rt = 0; rt < BM / 32; ++rt) {
     const _Float16* row = abuf + (rt * 32 + r) * kMmaARow + 32 * h;
@@ -601,6 +616,8 @@ __device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& R, const _Float
         c = mfma32(A[j], B[t][j], c);
       }
   }
+  mma_convert_b<BM, NTW>(Rn, Bn);
+  mma_store_a<BM, NTW>(Rn, abuf_n);
 }
 
 template <int BM, int NTW, int J16, int KS>
@@ -656,15 +673,20 @@ __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_e
   const MmaPtrs<BM, NTW> P = mma_ptrs<BM, NTW>(a, row0, col0, wt, lane);
   constexpr int RING = mma_ring<BM, NTW>();
   MmaRegs<BM, NTW> R[RING];
+  half8_t B[2][NTW][8];
 #pragma unroll
   for (int p = 0; p < RING; ++p) mma_load<BM, NTW>(R[p], P, a.D, KS * p + grp);
   mma_store_a<BM, NTW>(R[0], u.abuf[grp][0]);
+  mma_convert_b<BM, NTW>(R[0], B[0]);
   __syncthreads();
   for (int s0 = 0; s0 < nsteps; s0 += KS * RING) {
 #pragma unroll
     for (int p = 0; p < RING; ++p) {
-      mma_step<BM, NTW>(R[p], u.abuf[grp][p & 1], lane, acc);
-      mma_store_a<BM, NTW>(R[(p + 1) % RING], u.abuf[grp][(p + 1) & 1]);
+      // Step s0 + KS p + grp: MFMAs from tile p & 1 and B[p & 1]; the next
+      // step's conversion into the other tile and B[(p + 1) & 1]; then R[p]
+      // (fully used) reloads the step RING ahead.
+      mma_step<BM, NTW>(B[p & 1], u.abuf[grp][p & 1], R[(p + 1) % RING], B[(p + 1) & 1], u.abuf[grp][(p + 1) & 1],
+                        lane, acc);
       mma_load<BM, NTW>(R[p], P, a.D, s0 + KS * (p + RING) + grp);
       __syncthreads();
     }
