@@ -452,7 +452,7 @@ constexpr int kMmaThreads = 256;
 // accumulators and weight fragments of a wide tile already need most registers.
 template <int BM, int NTW>
 constexpr int mma_ring() {
-  return (BM / 32) * NTW >= 6 ? 2 : 4;
+  return (BM / 32) * NTW >= 6 ? 3 : 4;
 }
 constexpr int kMmaARow = 136;  // LDS row stride of the A tile in halves (128 values + 8 pad)
 
@@ -460,7 +460,7 @@ struct MmaArgs {
   TileArgs t;
   int ncb;     // expert blocks (workgroups per token block)
   int nwg;     // workgroups
-  int nsteps;  // 128-element K steps, rounded up to a multiple of 8 (K groups times any ring depth)
+  int nsteps;  // 128-element K steps, rounded up to a multiple of K groups times the ring depth
 };
 
 // Token rows per thread in the A tile (4 threads per row): one slot per 64
@@ -574,58 +574,85 @@ constexpr int mma_sets() {
   return (BM / 32) * NTW < 4 ? 2 : 1;
 }
 
-// B fragments of one step, converted from this lane's raw chunks.
+// One step: the MFMAs of step s with A from the LDS tile and B converted
+// from this step's raw chunks (Rc) just ahead of the MFMAs of the first row
+// tile that use it, interleaved with the conversion of step s + 1's A
+// chunks (Rn) into the other LDS tile. A wavefront issues one instruction
+// every few clocks while an MFMA keeps the matrix core busy for 32, so each
+// MFMA is followed by a share of the conversion units (8 elements each) and
+// scheduling fences keep that order. The A fragments of row tile rt + 1 are
+// read right after their last use in row tile rt.
 template <int BM, int NTW>
-__device__ __forceinline__ void mma_convert_b(const MmaRegs<BM, NTW>& R, half8_t (&B)[NTW][8]) {
+__device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& Rc, const _Float16* abuf, const MmaRegs<BM, NTW>& Rn,
+                                         _Float16* abuf_n, int lane,
+                                         f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
+  constexpr int NS = mma_sets<BM, NTW>();
+  constexpr int SL = mma_row_slots<BM>();
+  constexpr int NM = (BM / 32) * 8 * NTW;  // MFMAs; the first 8 NTW use B units 0 .. 8 NTW - 1 in order
+  constexpr int NB = 8 * NTW;              // B units
+  constexpr int NA = 4 * SL;               // A units
+  const int r = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x & (kMmaThreads - 1), q4 = tid & 3;
+  _Float16 bsc[NTW][2][2], asc[SL][2];
 #pragma unroll
   for (int t = 0; t < NTW; ++t)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const _Float16 s0 = e4m3_f16(R.bs[t][c] & 0xFFu), s1 = e4m3_f16(R.bs[t][c] >> 8);
-      B[t][4 * c + 0] = fp4x8_to_f16(R.b[t][c][0], s0);
-      B[t][4 * c + 1] = fp4x8_to_f16(R.b[t][c][1], s0);
-      B[t][4 * c + 2] = fp4x8_to_f16(R.b[t][c][2], s1);
-      B[t][4 * c + 3] = fp4x8_to_f16(R.b[t][c][3], s1);
+      bsc[t][c][0] = e4m3_f16(Rc.bs[t][c] & 0xFFu);
+      bsc[t][c][1] = e4m3_f16(Rc.bs[t][c] >> 8);
     }
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    asc[i][0] = e4m3_f16(Rn.as[i] & 0xFFu);
+    asc[i][1] = e4m3_f16(Rn.as[i] >> 8);
+  }
+  half8_t B[NTW][8];
+  // B unit m feeds MFMA m of the first row tile: K slice j = m / NTW of
+  // expert tile t = m % NTW.
+  auto bunit = [&](auto uc) {
+    constexpr int m = decltype(uc)::value, j = m / NTW, t = m % NTW;
+    B[t][j] = fp4x8_to_f16(Rc.b[t][j / 4][j % 4], bsc[t][j / 4][(j % 4) >> 1]);
+  };
+  auto aunit = [&](auto uc) {
+    constexpr int i = decltype(uc)::value / 4, q = decltype(uc)::value % 4;
+    const int row = (tid >> 2) + 64 * i;
+    if (BM >= 64 || row < BM)  // BM = 32: threads 128..255 hold no row
+      reinterpret_cast<half8_t*>(abuf_n + row * kMmaARow + 32 * q4)[q] = fp4x8_to_f16(Rn.a[i][q], asc[i][q >> 1]);
+  };
+  const _Float16* arow = abuf + r * kMmaARow + 32 * h;
+  auto afrag = [&](int rt, int j) {
+    return *reinterpret_cast<const half8_t*>(arow + rt * 32 * kMmaARow + (j < 4 ? 8 * j : 64 + 8 * (j - 4)));
+  };
+  half8_t A[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) A[j] = afrag(0, j);
+  bunit(IntC<0>{});
+  static_for<0, NM>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    constexpr int rt = m / (8 * NTW), j = (m / NTW) % 8, t = m % NTW;
+    f32x16_t& c = acc[NS == 2 ? (j >> 2) : 0][rt][t];
+    c = mfma32(A[j], B[t][j], c);
+    if constexpr (t == NTW - 1 && rt + 1 < BM / 32) A[j] = afrag(rt + 1, j);
+    if constexpr (m + 1 < NB) bunit(IntC<m + 1>{});
+    static_for<(m * NA + NM - 1) / NM, ((m + 1) * NA + NM - 1) / NM>(aunit);
+    __builtin_amdgcn_sched_barrier(0);
+  });
 }
 
-// One pipelined step: the MFMAs of step s (A from the LDS tile, B converted
-// the step before) with the conversion work of step s + 1 — its B fragments
-// into Bn and its A chunks into the other LDS tile — interleaved between
-// them (scheduling groups: one MFMA, then a few VALU instructions), so that
-// a single wavefront keeps both the matrix core and the VALU busy.
-template <int BM, int NTW>
-__device__ __forceinline__ void mma_step(const half8_t (&B)[NTW][8], const _Float16* abuf, const MmaRegs<BM, NTW>& Rn,
-                                         half8_t (&Bn)[NTW][8], _Float16* abuf_n, int lane,
-                                         f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
-  constexpr int NS = mma_sets<BM, NTW>();
-  const int r = lane & 31, h = lane >> 5;
-  // A fragments one 32-row tile at a time, each used against every expert
-  // tile; a tile's eight LDS reads are issued together.
-#pragma unroll
-  for (int rt = 0; rt < BM / 32; ++rt) {
-    const _Float16* row = abuf + (rt * 32 + r) * kMmaARow + 32 * h;
-    half8_t A[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) A[j] = *reinterpret_cast<const half8_t*>(row + (j < 4 ? 8 * j : 64 + 8 * (j - 4)));
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        f32x16_t& c = acc[NS == 2 ? (j >> 2) : 0][rt][t];
-        c = mfma32(A[j], B[t][j], c);
-      }
-  }
-  mma_convert_b<BM, NTW>(Rn, Bn);
-  mma_store_a<BM, NTW>(Rn, abuf_n);
-}
+// Epilogue rows per pass: 64 when two K groups share the work and the rows
+// fit the LDS, else 32. Each wavefront routes LR / (4 KS) rows per pass, as
+// sets of four.
+template <int BM, int J16, int KS>
+constexpr int epi_rows() { return KS == 2 && BM >= 64 && J16 <= 24 ? 64 : 32; }
+template <int BM, int J16, int KS>
+constexpr int epi_sets() { return KS == 2 ? epi_rows<BM, J16, KS>() / 32 : 1; }
 
 template <int BM, int NTW, int J16, int KS>
 union MmaLds {
   _Float16 abuf[KS][2][BM * kMmaARow];  // K loop: each K group's converted A tiles, double-buffered
   struct {
-    float lg[32 * (16 * J16 + 4)];      // epilogue: 32 tokens' logits at a time
-    Row16Scratch<J16> rsc[4 * KS];      // one router scratch per wavefront
+    float lg[epi_rows<BM, J16, KS>() * (16 * J16 + 4)];           // epilogue: one pass's logits
+    Row16Scratch<J16, epi_sets<BM, J16, KS>()> rsc[4 * KS];        // one router scratch per wavefront
   } epi;
 };
 
@@ -673,20 +700,20 @@ __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_e
   const MmaPtrs<BM, NTW> P = mma_ptrs<BM, NTW>(a, row0, col0, wt, lane);
   constexpr int RING = mma_ring<BM, NTW>();
   MmaRegs<BM, NTW> R[RING];
-  half8_t B[2][NTW][8];
 #pragma unroll
   for (int p = 0; p < RING; ++p) mma_load<BM, NTW>(R[p], P, a.D, KS * p + grp);
   mma_store_a<BM, NTW>(R[0], u.abuf[grp][0]);
-  mma_convert_b<BM, NTW>(R[0], B[0]);
   __syncthreads();
   for (int s0 = 0; s0 < nsteps; s0 += KS * RING) {
+    // The A tiles alternate with this group's step count, RING it + p: with
+    // an odd ring the parity of p alone does not alternate across passes.
+    const int par = (RING & 1) ? (s0 / (KS * RING)) & 1 : 0;
 #pragma unroll
     for (int p = 0; p < RING; ++p) {
-      // Step s0 + KS p + grp: MFMAs from tile p & 1 and B[p & 1]; the next
-      // step's conversion into the other tile and B[(p + 1) & 1]; then R[p]
+      // Step s0 + KS p + grp: A from tile (p + par) & 1, B from R[p]; the
+      // next step's A (R[(p + 1) % RING]) into the other tile; then R[p]
       // (fully used) reloads the step RING ahead.
-      mma_step<BM, NTW>(B[p & 1], u.abuf[grp][p & 1], R[(p + 1) % RING], B[(p + 1) & 1], u.abuf[grp][(p + 1) & 1],
-                        lane, acc);
+      mma_step<BM, NTW>(R[p], u.abuf[grp][(p + par) & 1], R[(p + 1) % RING], u.abuf[grp][(p + 1 + par) & 1], lane, acc);
       mma_load<BM, NTW>(R[p], P, a.D, s0 + KS * (p + RING) + grp);
       __syncthreads();
     }
@@ -705,17 +732,19 @@ __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_e
   const int r = lane & 31, h = lane >> 5;
   if ((int)threadIdx.x < E) bias_s[threadIdx.x] = bias0;
   if (KS == 1 && (int)threadIdx.x + 256 < E) bias_s[threadIdx.x + 256] = bias1;
-  // Pass rt: this K group's scaled sums of row tile rt into lg (group 1 first,
-  // then group 0 adds), columns local to the workgroup's expert block when
-  // `local`, else the expert index.
-  auto tile_to_lds = [&](auto rtc, bool local) {
+  // This K group's scaled sums of row tile rt into lg rows lr0 .. lr0 + 31
+  // (group 1 first, then group 0 adds); columns are local to the workgroup's
+  // expert block under split experts, else expert indexes (the same when
+  // there is one expert block).
+  auto tile_to_lds = [&](auto rtc, int lr0) {
     constexpr int rt = decltype(rtc)::value;
+    float* out = lg + lr0 * ldE;
     if (KS == 2 && grp == 1) {
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
         const int c = (wt + 4 * t) * 32 + r;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) lg[(8 * (v >> 2) + 4 * h + (v & 3)) * ldE + c] = acc[0][rt][t][v];
+        for (int v = 0; v < 16; ++v) out[(8 * (v >> 2) + 4 * h + (v & 3)) * ldE + c] = acc[0][rt][t][v];
       }
     }
     if (KS == 2) __syncthreads();
@@ -725,12 +754,11 @@ __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_e
         const int c = (wt + 4 * t) * 32 + r;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float* d = &lg[(8 * (v >> 2) + 4 * h + (v & 3)) * ldE + c];
+          float* d = &out[(8 * (v >> 2) + 4 * h + (v & 3)) * ldE + c];
           *d = (KS == 2 ? acc[0][rt][t][v] + *d : acc[0][rt][t][v]) * scale;
         }
       }
     }
-    (void)local;
   };
   if (m.ncb > 1) {
     // Split experts: this block's logits to the workspace, then the last
@@ -740,7 +768,7 @@ __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_e
       const int base = row0 + rt * 32;
       if (base >= a.T) return;  // uniform
       __syncthreads();
-      tile_to_lds(rtc, true);
+      tile_to_lds(rtc, 0);
       __syncthreads();
       const int nrows = min(32, a.T - base);
       for (int i = threadIdx.x; i < 32 * 128 * NTW; i += kMmaThreads * KS) {
@@ -755,55 +783,69 @@ __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_e
     static_for<0, BM / 32>(store_pass);
     if (!arrive_last(&a.counters[rb], m.ncb, &s_last)) return;
   }
-  // Passes of 32 tokens; a compile-time row tile index keeps the accumulator
+  // Passes of LR tokens; compile-time row tile indexes keep the accumulator
   // indexes static (a runtime loop over this body would put them in scratch).
-  auto pass = [&](auto rtc) {
-    constexpr int rt = decltype(rtc)::value;
-    const int base = row0 + rt * 32;
+  constexpr int LR = epi_rows<BM, J16, KS>(), NSET = epi_sets<BM, J16, KS>();
+  auto pass = [&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    const int base = row0 + p * LR;
     if (base >= a.T) return;  // uniform
+    const int nrows = min(LR, a.T - base);
     __syncthreads();
     if (m.ncb > 1) {
       // Gather the token block's logits from every expert block: wavefront w
       // takes rows w, w + 4KS, ...; lane l columns l, l + 64, ...; all loads
-      // are issued before the first store.
-      const int nrows = min(32, a.T - base);
-      constexpr int RR = 32 / (4 * KS);
+      // are issued before the first store. Rows past T and experts past E
+      // read a clamped (valid) address; the router masks both.
+      constexpr int RR = LR / (4 * KS);
+      const float* src = a.lbuf + (int64_t)base * E;
       float v[RR][J16 / 4];
 #pragma unroll
       for (int rr = 0; rr < RR; ++rr)
 #pragma unroll
         for (int cc = 0; cc < J16 / 4; ++cc) {
-          const int mm = wave + 4 * KS * rr, e = lane + 64 * cc;
-          v[rr][cc] = (mm < nrows && e < E) ? load_coherent(a.lbuf + (int64_t)(base + mm) * E + e) : 0.0f;
+          const int mm = min(wave + 4 * KS * rr, nrows - 1), e = min(lane + 64 * cc, E - 1);
+          v[rr][cc] = load_coherent(src + mm * E + e);
         }
 #pragma unroll
       for (int rr = 0; rr < RR; ++rr)
 #pragma unroll
-        for (int cc = 0; cc < J16 / 4; ++cc) {
-          const int mm = wave + 4 * KS * rr, e = lane + 64 * cc;
-          if (mm < nrows && e < E) lg[mm * ldE + e] = v[rr][cc];
-        }
+        for (int cc = 0; cc < J16 / 4; ++cc) lg[(wave + 4 * KS * rr) * ldE + lane + 64 * cc] = v[rr][cc];
     } else {
-      tile_to_lds(rtc, false);
+      static_for<0, LR / 32>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        tile_to_lds(IntC<p * (LR / 32) + i>{}, 32 * i);
+      });
     }
     __syncthreads();
-    // 32 rows: wavefront w routes rows (32 / 4KS) w .. , four at a time.
+    // Wavefront w routes rows RW w .. RW w + RW - 1 (RW = LR / 4KS), in calls
+    // of NSET interleaved sets of four.
+    constexpr int RW = LR / (4 * KS);
 #pragma unroll
-    for (int q = 0; q < 2 / KS; ++q) {
-      const int mm = wave * (8 / KS) + q * 4 + (lane >> 4);
-      const int64_t t = base + mm;
-      row16_route<J16>(lg + mm * ldE, bias_s, E, a.k, a.routed_scale, t < a.T, a.idx + t * a.k, a.w + t * a.k,
-                       u.epi.rsc[wave]);
+    for (int c0 = 0; c0 < RW / 4; c0 += NSET) {
+      const float* Lr[NSET];
+      bool vr[NSET];
+      int32_t* oi[NSET];
+      float* ow[NSET];
+#pragma unroll
+      for (int q = 0; q < NSET; ++q) {
+        const int mm = wave * RW + 4 * (c0 + q) + (lane >> 4);
+        const int64_t t = base + mm;
+        Lr[q] = lg + mm * ldE;
+        vr[q] = t < a.T;
+        oi[q] = a.idx + t * a.k;
+        ow[q] = a.w + t * a.k;
+      }
+      row16_route<J16, NSET>(Lr, bias_s, E, a.k, a.routed_scale, vr, oi, ow, u.epi.rsc[wave]);
     }
     if (a.logits_out && m.ncb == 1) {
-      const int nrows = min(32, a.T - base);
       for (int i = threadIdx.x; i < nrows * E; i += kMmaThreads * KS) {
         const int mm = i / E, e = i - mm * E;
         a.logits_out[(int64_t)(base + mm) * E + e] = lg[mm * ldE + e];
       }
     }
   };
-  static_for<0, BM / 32>(pass);
+  static_for<0, BM / LR>(pass);
   if (m.ncb > 1) release_counter(&a.counters[rb]);
 }
 
@@ -906,8 +948,10 @@ constexpr int mma_ksplit() {
 }
 
 template <int BM, int NTW, int J16>
-static hipError_t launch_mma_t(const MmaArgs& m, hipStream_t stream) {
-  constexpr int KS = mma_ksplit<BM, NTW>();
+static hipError_t launch_mma_t(const MmaArgs& m0, hipStream_t stream) {
+  constexpr int KS = mma_ksplit<BM, NTW>(), G = KS * mma_ring<BM, NTW>();
+  MmaArgs m = m0;
+  m.nsteps = (m0.nsteps + G - 1) / G * G;
   gate_mfma_kernel<BM, NTW, J16, KS><<<m.nwg, kMmaThreads * KS, 0, stream>>>(m);
   return hipGetLastError();
 }
@@ -924,7 +968,7 @@ static hipError_t launch_mma_j(const MmaArgs& m, hipStream_t stream) {
 
 static hipError_t launch_mma(const TileArgs& a, hipStream_t stream) {
   const MmaPlan p = plan_mma(a.T, a.E);
-  MmaArgs m{a, p.ncb, 0, (int)((a.D + 128 * 8 - 1) / (128 * 8)) * 8};
+  MmaArgs m{a, p.ncb, 0, (int)((a.D + 127) / 128)};
   m.nwg = (int)((a.T + p.bm - 1) / p.bm) * p.ncb;
   switch (p.bm * 8 + p.ntw) {
     case 128 * 8 + 1: return launch_mma_j<128, 1>(m, stream);

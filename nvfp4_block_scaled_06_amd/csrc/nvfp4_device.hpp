@@ -533,10 +533,13 @@ __device__ __forceinline__ void wave_route_row(const float* Lrow, const float* b
 //     sum is a DPP row sum and each chosen lane stores its output at its rank.
 constexpr int kRow16MaxSurvivors = 32;
 
-template <int J16>
+// Entry kRow16MaxSurvivors of each row is a spare slot that absorbs the
+// writes of non-surviving keys, so compaction needs no branch per key. One
+// scratch serves NSET sets of four rows.
+template <int J16, int NSET>
 struct Row16Scratch {
-  uint64_t cand[4][kRow16MaxSurvivors];
-  float cs[4][kRow16MaxSurvivors];
+  uint64_t cand[NSET][4][kRow16MaxSurvivors + 1];
+  float cs[NSET][4][kRow16MaxSurvivors + 1];
 };
 
 __device__ __forceinline__ uint32_t row_min_u32(uint32_t v) {
@@ -579,145 +582,186 @@ __device__ __forceinline__ int count_above(uint32_t v, int n) {
   return n;
 }
 
-// Survivors 0..NS-1 of a row (entries past the count are zero), ranked and
-// stored; NS = 16 or 32, lane l16 takes survivors l16 and l16 + 16.
-template <int J16, int NS>
-__device__ __forceinline__ void row16_rank_store(int C, int k, float routed_scale, bool valid, int l16, int rq,
-                                                 int32_t* __restrict__ out_idx, float* __restrict__ out_w,
-                                                 const Row16Scratch<J16>& sc) {
-  uint64_t all[NS];
+// Survivors 0..NS-1 of each row (entries past the count are zero), ranked
+// and stored; NS = 16 or 32, lane l16 takes survivors l16 and l16 + 16.
+template <int J16, int NSET, int NS>
+__device__ __forceinline__ void row16_rank_store(const int (&C)[NSET], int k, float routed_scale,
+                                                 const bool (&valid)[NSET], int l16, int rq,
+                                                 int32_t* const (&out_idx)[NSET], float* const (&out_w)[NSET],
+                                                 const Row16Scratch<J16, NSET>& sc) {
+  uint64_t mine[NSET][NS / 16];
+  float ms[NSET][NS / 16];
+  int rank[NSET][NS / 16];
 #pragma unroll
-  for (int u = 0; u < NS; ++u) all[u] = sc.cand[rq][u];
-  uint64_t mine[NS / 16];
-  float ms[NS / 16];
-  int rank[NS / 16];
+  for (int r = 0; r < NSET; ++r)
 #pragma unroll
-  for (int h = 0; h < NS / 16; ++h) {
-    mine[h] = sc.cand[rq][l16 + 16 * h];
-    ms[h] = sc.cs[rq][l16 + 16 * h];
-    rank[h] = 0;
-  }
+    for (int h = 0; h < NS / 16; ++h) {
+      mine[r][h] = sc.cand[r][rq][l16 + 16 * h];
+      ms[r][h] = sc.cs[r][rq][l16 + 16 * h];
+      rank[r][h] = 0;
+    }
 #pragma unroll
   for (int u = 0; u < NS; ++u)
 #pragma unroll
-    for (int h = 0; h < NS / 16; ++h) rank[h] += all[u] > mine[h] ? 1 : 0;
-  float part = 0.0f;
-  bool chosen[NS / 16];
+    for (int r = 0; r < NSET; ++r) {
+      const uint64_t other = sc.cand[r][rq][u];
 #pragma unroll
-  for (int h = 0; h < NS / 16; ++h) {
-    chosen[h] = l16 + 16 * h < C && rank[h] < k;
-    part += chosen[h] ? ms[h] : 0.0f;
+      for (int h = 0; h < NS / 16; ++h) rank[r][h] += other > mine[r][h] ? 1 : 0;
+    }
+  float part[NSET];
+  bool chosen[NSET][NS / 16];
+#pragma unroll
+  for (int r = 0; r < NSET; ++r) {
+    part[r] = 0.0f;
+#pragma unroll
+    for (int h = 0; h < NS / 16; ++h) {
+      chosen[r][h] = l16 + 16 * h < C[r] && rank[r][h] < k;
+      part[r] += chosen[r][h] ? ms[r][h] : 0.0f;
+    }
   }
-  const float f = routed_scale * __builtin_amdgcn_rcpf(row_sum(part));
-  if (valid) {
+#pragma unroll
+  for (int r = 0; r < NSET; ++r) {
+    const float f = routed_scale * __builtin_amdgcn_rcpf(row_sum(part[r]));
 #pragma unroll
     for (int h = 0; h < NS / 16; ++h)
-      if (chosen[h]) {
-        out_idx[rank[h]] = (int)(0xFFFFFFFFu - (uint32_t)mine[h]);
-        out_w[rank[h]] = ms[h] * f;
+      if (valid[r] && chosen[r][h]) {
+        out_idx[r][rank[r][h]] = (int)(0xFFFFFFFFu - (uint32_t)mine[r][h]);
+        out_w[r][rank[r][h]] = ms[r][h] * f;
       }
   }
 }
 
-template <int J16>
-__device__ __forceinline__ void row16_route(const float* Lrow, const float* bias_lds, int E, int k,
-                                            float routed_scale, bool valid, int32_t* __restrict__ out_idx,
-                                            float* __restrict__ out_w, Row16Scratch<J16>& sc) {
+// Largest per-row survivor count over the four rows of every set.
+template <int NSET>
+__device__ __forceinline__ int rows_max(const int (&C)[NSET]) {
+  int m = 0;
+#pragma unroll
+  for (int r = 0; r < NSET; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m = max(m, (int)__builtin_amdgcn_readlane(C[r], 16 * q));
+  return m;
+}
+
+// Routes NSET independent sets of four rows at once (lane l16 of row group
+// rq of set r reads Lrow[r]); the sets' instruction streams interleave, which
+// hides the latency of each set's dependent steps.
+template <int J16, int NSET>
+__device__ __forceinline__ void row16_route(const float* const (&Lrow)[NSET], const float* bias_lds, int E, int k,
+                                            float routed_scale, const bool (&valid)[NSET],
+                                            int32_t* const (&out_idx)[NSET], float* const (&out_w)[NSET],
+                                            Row16Scratch<J16, NSET>& sc) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, rq = lane >> 4;
   const int e0 = l16 * J16;
-  uint32_t key[J16];
-  float s[J16];
-  uint32_t lm = 0u;
+  uint32_t key[NSET][J16];
+  float s[NSET][J16];
+  uint32_t lm[NSET];
+#pragma unroll
+  for (int r = 0; r < NSET; ++r) lm[r] = 0u;
 #pragma unroll
   for (int j4 = 0; j4 < J16 / 4; ++j4) {
-    const float4 L4 = *reinterpret_cast<const float4*>(Lrow + e0 + 4 * j4);
     const float4 B4 = *reinterpret_cast<const float4*>(bias_lds + e0 + 4 * j4);
-    const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Bv[4] = {B4.x, B4.y, B4.z, B4.w};
+    const float Bv[4] = {B4.x, B4.y, B4.z, B4.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 4 * j4 + i;
-      s[j] = sigmoid_fast(Lv[i]);
-      key[j] = (e0 + j < E && valid) ? score_key(s[j] + Bv[i]) : 0u;
-      lm = max(lm, key[j]);
+    for (int r = 0; r < NSET; ++r) {
+      const float4 L4 = *reinterpret_cast<const float4*>(Lrow[r] + e0 + 4 * j4);
+      const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * j4 + i;
+        s[r][j] = sigmoid_fast(Lv[i]);
+        key[r][j] = (e0 + j < E && valid[r]) ? score_key(s[r][j] + Bv[i]) : 0u;
+        lm[r] = max(lm[r], key[r][j]);
+      }
     }
   }
   // Survivor rule: a nonzero key > hi, or == hi among this lane's first
   // `ties` such keys (the bound: hi = tau - 1, no ties taken; the exact
   // search: hi = K, ties shared out in index order).
-  uint32_t hi = 0u;
-  int ties = 0x7FFFFFFF;
-  int C = kRow16MaxSurvivors + 1;
-  if (k <= 16) {
-    const int above = count_above<1>(lm, 0);
-    const uint32_t tau = row_min_u32(above < k ? lm : 0xFFFFFFFFu);
-    int cnt = 0;
+  uint32_t hi[NSET];
+  int ties[NSET], C[NSET];
 #pragma unroll
-    for (int j = 0; j < J16; ++j) cnt += (key[j] != 0u && key[j] >= tau) ? 1 : 0;
-    C = row_sum_i(cnt);
-    hi = tau > 0u ? tau - 1u : 0u;  // key > hi <=> key >= tau, for the nonzero keys
-    ties = 0;
+  for (int r = 0; r < NSET; ++r) {
+    hi[r] = 0u;
+    ties[r] = 0x7FFFFFFF;
+    C[r] = kRow16MaxSurvivors + 1;
   }
-  int cmax = C;
-  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 0));
-  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 16));
-  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 32));
-  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 48));
-  if (cmax > kRow16MaxSurvivors) {
-    // Exact k-th largest key K of each row, bit by bit: the largest t with at
-    // least k keys >= t.
-    uint32_t K = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t t = K | (1u << bit);
+  if (k <= 16) {
+#pragma unroll
+    for (int r = 0; r < NSET; ++r) {
+      const int above = count_above<1>(lm[r], 0);
+      const uint32_t tau = row_min_u32(above < k ? lm[r] : 0xFFFFFFFFu);
       int cnt = 0;
 #pragma unroll
-      for (int j = 0; j < J16; ++j) cnt += key[j] >= t ? 1 : 0;
-      if (row_sum_i(cnt) >= k) K = t;
+      for (int j = 0; j < J16; ++j) cnt += (key[r][j] != 0u && key[r][j] >= tau) ? 1 : 0;
+      C[r] = row_sum_i(cnt);
+      hi[r] = tau > 0u ? tau - 1u : 0u;  // key > hi <=> key >= tau, for the nonzero keys
+      ties[r] = 0;
     }
-    int gt = 0, eq = 0;
+  }
+  if (rows_max<NSET>(C) > kRow16MaxSurvivors) {
+    // Exact k-th largest key K of each row, bit by bit: the largest t with at
+    // least k keys >= t.
+    uint32_t K[NSET];
 #pragma unroll
-    for (int j = 0; j < J16; ++j) {
-      gt += key[j] > K ? 1 : 0;
-      eq += (key[j] == K && key[j] != 0u) ? 1 : 0;
+    for (int r = 0; r < NSET; ++r) K[r] = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+      for (int r = 0; r < NSET; ++r) {
+        const uint32_t t = K[r] | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < J16; ++j) cnt += key[r][j] >= t ? 1 : 0;
+        if (row_sum_i(cnt) >= k) K[r] = t;
+      }
     }
-    hi = K;
-    ties = k - row_sum_i(gt);                 // equal keys still to take, lowest index first
-    const int eq_before = row_scan(eq) - eq;  // equal keys in lanes before this one
-    ties -= eq_before;                        // this lane may take its first `ties` equal keys
-    C = k;
+#pragma unroll
+    for (int r = 0; r < NSET; ++r) {
+      int gt = 0, eq = 0;
+#pragma unroll
+      for (int j = 0; j < J16; ++j) {
+        gt += key[r][j] > K[r] ? 1 : 0;
+        eq += (key[r][j] == K[r] && key[r][j] != 0u) ? 1 : 0;
+      }
+      hi[r] = K[r];
+      ties[r] = k - row_sum_i(gt);                 // equal keys still to take, lowest index first
+      ties[r] -= row_scan(eq) - eq;                // minus equal keys in lanes before this one
+      C[r] = k;
+    }
   }
   // Compact the survivors (at most 32 per row).
-  int cnt = 0, teq = 0;
-  bool surv[J16];
 #pragma unroll
-  for (int j = 0; j < J16; ++j) {
-    const bool eq = key[j] == hi && key[j] != 0u;
-    surv[j] = key[j] != 0u && (key[j] > hi || (eq && teq < ties));
-    teq += eq ? 1 : 0;
-    cnt += surv[j] ? 1 : 0;
-  }
-  int pos = row_scan(cnt) - cnt;
+  for (int r = 0; r < NSET; ++r) {
+    int cnt = 0, teq = 0;
+    bool surv[J16];
 #pragma unroll
-  for (int j = 0; j < J16; ++j) {
-    if (surv[j]) {
-      sc.cand[rq][pos] = ((uint64_t)key[j] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(e0 + j));
-      sc.cs[rq][pos] = s[j];
-      ++pos;
+    for (int j = 0; j < J16; ++j) {
+      const bool eq = key[r][j] == hi[r] && key[r][j] != 0u;
+      surv[j] = key[r][j] != 0u && (key[r][j] > hi[r] || (eq && teq < ties[r]));
+      teq += eq ? 1 : 0;
+      cnt += surv[j] ? 1 : 0;
     }
+    int pos = row_scan(cnt) - cnt;
+#pragma unroll
+    for (int j = 0; j < J16; ++j) {
+      const int slot = surv[j] ? pos : kRow16MaxSurvivors;
+      sc.cand[r][rq][slot] = ((uint64_t)key[r][j] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(e0 + j));
+      sc.cs[r][rq][slot] = s[r][j];
+      pos += surv[j] ? 1 : 0;
+    }
+    C[r] = row_sum_i(cnt);
   }
-  C = row_sum_i(cnt);
-  cmax = C;
-  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 0));
-  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 16));
-  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 32));
-  cmax = max(cmax, (int)__builtin_amdgcn_readlane(C, 48));
-  const int ns = cmax <= 16 ? 16 : 32;
-  if (C <= l16) sc.cand[rq][l16] = 0ull;  // entries past the count rank below everything
-  if (ns == 32 && C <= l16 + 16) sc.cand[rq][l16 + 16] = 0ull;
+  const int ns = rows_max<NSET>(C) <= 16 ? 16 : 32;
+  // Entries past the count rank below everything.
+#pragma unroll
+  for (int r = 0; r < NSET; ++r) {
+    sc.cand[r][rq][C[r] <= l16 ? l16 : kRow16MaxSurvivors] = 0ull;
+    if (ns == 32) sc.cand[r][rq][C[r] <= l16 + 16 ? l16 + 16 : kRow16MaxSurvivors] = 0ull;
+  }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (ns == 16) row16_rank_store<J16, 16>(C, k, routed_scale, valid, l16, rq, out_idx, out_w, sc);
-  else row16_rank_store<J16, 32>(C, k, routed_scale, valid, l16, rq, out_idx, out_w, sc);
+  if (ns == 16) row16_rank_store<J16, NSET, 16>(C, k, routed_scale, valid, l16, rq, out_idx, out_w, sc);
+  else row16_rank_store<J16, NSET, 32>(C, k, routed_scale, valid, l16, rq, out_idx, out_w, sc);
 }
 
 }  // namespace nvr
