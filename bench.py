@@ -44,14 +44,17 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_forward_T1_D7168_E256_k8_traffic.txt")
 
 
+# Every source the decode kernel's translation unit is built from.
+DECODE_SOURCES = ("gate_decode.hip", "gate_common.hpp", "nvfp4_device.hpp", "router_internal.hpp")
+
+
 def kernel_source_hash():
-    """sha256 over the HIP sources, so a stale counter summary is not reported for a changed kernel."""
+    """sha256 over the decode kernel's sources, so a stale counter summary is not reported for a changed kernel."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "nvfp4_block_scaled_06_amd", "csrc")
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".hpp")):
-            h.update(name.encode())
-            h.update(open(os.path.join(d, name), "rb").read())
+    for name in DECODE_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(d, name), "rb").read())
     return h.hexdigest()
 
 

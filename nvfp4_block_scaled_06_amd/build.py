@@ -8,14 +8,13 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4_router.so")
-SOURCES = ["router_api.hip", "quantize.hip", "gate.hip"]
+SOURCES = ["router_api.hip", "quantize.hip", "gate.hip", "gate_decode.hip"]
 
-FLAGS = [
+COMPILE_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # Packed fp32 arithmetic stays off: hipcc would otherwise form
     # v_pk_{add,mul,fma}_f32 from plain float code.
@@ -31,10 +30,23 @@ def hipcc():
 
 
 def build(verbose=False, extra_flags=()):
-    """Compile every HIP source into the shared library; returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every HIP source (one hipcc process each, in parallel) and link
+    the shared library; returns its path."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    procs, objs = [], []
+    for s in SOURCES:
+        obj = os.path.join(objdir, s.replace(".hip", ".o"))
+        cmd = [hipcc()] + COMPILE_FLAGS + list(extra_flags) + ["-c", os.path.join(CSRC, s), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd), s))
+        objs.append(obj)
+    failed = [s for p, s in procs if p.wait() != 0]
+    if failed:
+        raise RuntimeError("hipcc failed on " + ", ".join(failed))
     tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + list(extra_flags) + srcs + ["-o", tmp]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

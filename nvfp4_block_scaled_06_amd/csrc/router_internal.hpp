@@ -51,6 +51,15 @@ hipError_t launch_gate(const uint8_t* x_codes, const uint8_t* x_scales, const fl
                        int64_t D, int64_t E, int64_t k, int32_t* topk_idx, float* topk_w, float* logits_out,
                        uint32_t* counters, void* scratch, hipStream_t stream);
 
+// Decode-size gate (gate_decode.hip): whether T x D takes it, its scratch,
+// and its launch (reading quantized x).
+bool decode_fits(int64_t T, int64_t D);
+size_t decode_scratch_bytes(int64_t T, int64_t D, int64_t E);
+hipError_t launch_decode_gate(const uint8_t* x_codes, const uint8_t* x_scales, const float* gsa,
+                              const uint8_t* w_codes, const uint8_t* w_scales, const float* gsw, const float* bias,
+                              float routed_scale, int64_t T, int64_t D, int64_t E, int64_t k, int32_t* topk_idx,
+                              float* topk_w, float* logits_out, float* lbuf, uint32_t* counters, hipStream_t stream);
+
 // Quantize + gate in one launch (decode-size T only; see forward_single_launch).
 bool forward_single_launch(int64_t T, int64_t D);
 hipError_t launch_forward_fused(const void* x, const float* gsa_override, uint8_t* x_codes, uint8_t* x_scales,
