@@ -279,7 +279,7 @@ def main():
         achieved = gate_flops(c) / tg / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None,
-                "kernel": "gate_fused_kernel" if c.T > 256 else "gate_tile_kernel",
+                "kernel": "gate_mfma_kernel" if c.T > 256 else "gate_tile_kernel",
                 "algorithmic": f"{gate_flops(c)} FLOP per launch"}
     else:
         # One launch per step: the events around the timed replay give the average launch duration.

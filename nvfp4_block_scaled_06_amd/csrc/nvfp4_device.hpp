@@ -96,38 +96,45 @@ __device__ __forceinline__ uint32_t sign_codes4(const uint32_t* w) {
 //     q there is no threshold other than v itself.
 //  2. r = |x| - v S gsa by one fma has the exact sign of q - v: v S is exact
 //     (at most 7 significant bits) and every term is a multiple of
-//     2^-31 v S gsa, far above the fp32 underflow threshold in this range.
-//     A nonzero r is at least that large, so r * 2^20 inv moves v by at
-//     least 2^-12 v.
-//  3. v is moved toward q by at most 2^-11 v: a threshold then converts to
-//     the code on q's side, an exact tie (r = 0) stays on the threshold and
-//     converts to the even code, and any other v keeps its own code.
+//     2^-31 v S gsa, far above the fp32 underflow threshold in this range,
+//     so the fma's one rounding cannot reach or cross zero. r is never -0
+//     (|x| >= 0, and an exact zero sum rounds to +0), so its bit pattern
+//     read as an integer and clamped to [-1, 1] is the sign of q - v.
+//  3. v moves toward q by 2^12 units in its last place (between 2^-12 v and
+//     2^-11 v; one shift-add on the bit pattern): a threshold then converts
+//     to the code on q's side, an exact tie (r = 0) stays on the threshold
+//     and converts to the even code, and any other v keeps its own code.
+//     When v = 0 (q = 0, or a zero scale with inv = 0) r >= 0, and the move
+//     gives a tiny positive value that converts to code 0.
 // The sign is copied from x last, so -0 and tiny negatives keep their sign.
-__device__ __forceinline__ float e2m1_exact_input(float x, float inv, float minv, float S, float gsa) {
+__device__ __forceinline__ float e2m1_exact_input(float x, float inv, float S, float gsa) {
   const float xa = fabsf(x);
   const float qa = fminf(xa * inv, 7.0f);
-  const float v = __uint_as_float((__float_as_uint(qa) + 0x100000u) & 0xFFE00000u);
-  const float r = fmaf(-(v * S), gsa, xa);
-  const float w = __builtin_amdgcn_fmed3f(fmaf(r, minv, v), v * 0x1.ffep-1f, v * 0x1.001p+0f);
-  return __uint_as_float((__float_as_uint(w) & 0x7FFFFFFFu) | (__float_as_uint(x) & 0x80000000u));
+  const uint32_t vb = (__float_as_uint(qa) + 0x100000u) & 0xFFE00000u;
+  const float r = fmaf(-(__uint_as_float(vb) * S), gsa, xa);
+  // One v_med3_i32 (the compiler would otherwise lower the clamp to two
+  // compare/select pairs).
+  int sgn;
+  asm("v_med3_i32 %0, %1, -1, 1" : "=v"(sgn) : "v"(__float_as_uint(r)));
+  const uint32_t wb = vb + ((uint32_t)sgn << 12);
+  return __uint_as_float((wb & 0x7FFFFFFFu) | (__float_as_uint(x) & 0x80000000u));
 }
 
 // One bf16 pair rounded to two E2M1 codes, written into byte I of `old`: the
 // even element in the low nibble.
 template <int I>
-__device__ __forceinline__ uint32_t fp4_exact_pair(uint32_t old, uint32_t w, float inv, float minv, float S,
-                                                   float gsa) {
-  const float a = e2m1_exact_input(bf16_lo(w), inv, minv, S, gsa);
-  const float b = e2m1_exact_input(bf16_hi(w), inv, minv, S, gsa);
+__device__ __forceinline__ uint32_t fp4_exact_pair(uint32_t old, uint32_t w, float inv, float S, float gsa) {
+  const float a = e2m1_exact_input(bf16_lo(w), inv, S, gsa);
+  const float b = e2m1_exact_input(bf16_hi(w), inv, S, gsa);
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, I);
 }
 
-__device__ __forceinline__ uint32_t fp4_exact8(const uint32_t* w, float inv, float minv, float S, float gsa) {
+__device__ __forceinline__ uint32_t fp4_exact8(const uint32_t* w, float inv, float S, float gsa) {
   uint32_t o = 0;
-  o = fp4_exact_pair<0>(o, w[0], inv, minv, S, gsa);
-  o = fp4_exact_pair<1>(o, w[1], inv, minv, S, gsa);
-  o = fp4_exact_pair<2>(o, w[2], inv, minv, S, gsa);
-  o = fp4_exact_pair<3>(o, w[3], inv, minv, S, gsa);
+  o = fp4_exact_pair<0>(o, w[0], inv, S, gsa);
+  o = fp4_exact_pair<1>(o, w[1], inv, S, gsa);
+  o = fp4_exact_pair<2>(o, w[2], inv, S, gsa);
+  o = fp4_exact_pair<3>(o, w[3], inv, S, gsa);
   return o;
 }
 
@@ -187,7 +194,7 @@ __device__ __forceinline__ uint32_t e4m3_byte_exact(float bmax, float p, float g
 // double result rounds like the exact one.
 struct BlockScale {
   uint32_t sbyte;
-  float S, inv, minv;
+  float S, inv;
   double G64;  // gsa * S, exact (slow path)
   bool fast;
 };
@@ -204,7 +211,6 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t m, float gsa) {
   }
   b.S = e4m3_value(b.sbyte);
   b.inv = (b.fast && b.S > 0.0f) ? __builtin_amdgcn_rcpf(gsa * b.S) : 0.0f;
-  b.minv = b.inv * 0x1p20f;
   b.G64 = (double)gsa * (double)b.S;
   return b;
 }
@@ -212,7 +218,7 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t m, float gsa) {
 // Codes of 8 elements (four bf16 pairs) under block scale b, packed as the
 // quantizer packs them (element 2i in the low nibble of byte i).
 __device__ __forceinline__ uint32_t encode8(const uint32_t* w, const BlockScale& b, float gsa) {
-  if (b.fast) return fp4_exact8(w, b.inv, b.minv, b.S, gsa);
+  if (b.fast) return fp4_exact8(w, b.inv, b.S, gsa);
   if (b.S == 0.0f) return sign_codes4(w);
   uint32_t out = 0u;
 #pragma unroll

@@ -15,7 +15,8 @@
 //  * large tensors: amax_partial_kernel writes one max per workgroup, then
 //    quant_kernel folds those partial maxima in every workgroup (a few KB from
 //    L2), derives the same gsa everywhere and quantizes (x read twice: a
-//    tensor-wide max has to be known before the first code is written).
+//    tensor-wide max has to be known before the first code is written; up to
+//    160 MB the second read comes from the Infinity Cache).
 #include "nvfp4_device.hpp"
 #include "router_internal.hpp"
 
@@ -95,6 +96,18 @@ __global__ __launch_bounds__(kSingleThreads) void quant_single_kernel(const u32x
 constexpr int kAmaxThreads = 256;
 constexpr int kAmaxUnroll = 4;
 
+// Tensors up to this size are read by the max pass with ordinary loads, so
+// that they stay in the 256 MB Infinity Cache for the quantize pass; larger
+// ones would only evict each other there and stream with nontemporal loads.
+constexpr int64_t kAmaxCachedBytes = 160ll << 20;
+
+template <bool NT>
+__device__ __forceinline__ u32x4_t amax_load(const u32x4_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const u32x4_t* __restrict__ x, int64_t nvec,
                                                                     uint32_t* __restrict__ partial) {
   __shared__ uint32_t red[kAmaxThreads / 64];
@@ -104,12 +117,12 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const u32x4_
   for (; i + (kAmaxUnroll - 1) * stride < nvec; i += kAmaxUnroll * stride) {
     u32x4_t v[kAmaxUnroll];
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = __builtin_nontemporal_load(x + i + u * stride);
+    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = amax_load<NT>(x + i + u * stride);
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) m = max(m, vec_absmax(v[u]));
   }
   for (; i < nvec; i += stride) {
-    m = max(m, vec_absmax(__builtin_nontemporal_load(x + i)));
+    m = max(m, vec_absmax(amax_load<NT>(x + i)));
   }
   m = block_max_u32(m, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
@@ -167,7 +180,10 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t D, const float* 
     const int64_t nvec = nblocks * 2;
     const int64_t want = (nvec + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
     npartial = (int)(want < kAmaxPartials ? (want < 1 ? 1 : want) : kAmaxPartials);
-    amax_partial_kernel<<<npartial, kAmaxThreads, 0, stream>>>(xv, nvec, partial);
+    if (nvec * 16 <= kAmaxCachedBytes)
+      amax_partial_kernel<false><<<npartial, kAmaxThreads, 0, stream>>>(xv, nvec, partial);
+    else
+      amax_partial_kernel<true><<<npartial, kAmaxThreads, 0, stream>>>(xv, nvec, partial);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
