@@ -152,6 +152,52 @@ def copy_calibration(torch, mib, reps):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": reps}), flush=True)
 
 
+def probe_rates(torch, rt, c, nbytes, time_graph, t_launch, eager):
+    """What a kernel that only reads can reach: the library's streaming-read probe over a footprint of the
+    gate's algorithmic bytes, cycled over as many buffers as there are layer sets and replayed like the
+    router (the achievable rate for this footprint), and over 1 GiB (the achievable HBM bandwidth)."""
+    dev = torch.device("cuda:0")
+    fb = (nbytes + 15) // 16 * 16
+    gen = torch.Generator(device=dev).manual_seed(0)
+    bufs = [torch.randint(0, 256, (fb,), dtype=torch.uint8, device=dev, generator=gen) for _ in range(c.layers)]
+    sink = torch.empty(8192, dtype=torch.int32, device=dev)
+
+    def step_probe(i):
+        rt.probe_read(bufs[i % len(bufs)], sink)
+
+    for i in range(20):
+        step_probe(i)
+    torch.cuda.synchronize()
+    if eager:
+        cur = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for i in range(200):
+            step_probe(i)
+        e1.record(cur)
+        torch.cuda.synchronize()
+        t_small = e0.elapsed_time(e1) * 1e-3 / 200
+    else:
+        _, ev = time_graph(step_probe)
+        t_small = ev / time_graph.steps
+    big = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    rt.probe_read(big, sink)
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in ev:
+        a.record(cur)
+        rt.probe_read(big, sink)
+        b.record(cur)
+    torch.cuda.synchronize()
+    t_big = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    del big, bufs
+    log(f"probe: {fb} B in {t_small * 1e6:.2f} us per launch; 1 GiB at {(1 << 30) / t_big / 1e9:.0f} GB/s")
+    return {"kernel": "probe_read_kernel", "footprint_bytes": fb, "buffers": c.layers,
+            "launch_us": t_small * 1e6, "achievable_gbs": fb / t_small / 1e9,
+            "frac_of_achievable": t_small / t_launch, "hbm_1gib_gbs": (1 << 30) / t_big / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +285,8 @@ def main():
         del g
         return dt, e0.elapsed_time(e1) * 1e-3
 
+    time_graph.steps = K
+
     for step in (step_forward, step_two_calls):
         for i in range(W):
             step(i)
@@ -291,7 +339,8 @@ def main():
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel": "gate_decode_kernel (quantizing; the whole call is one launch)",
                 "launch_us": t_launch * 1e6,
-                "algorithmic": f"{nbytes} B per launch"}
+                "algorithmic": f"{nbytes} B per launch",
+                "probe": probe_rates(torch, rt, c, nbytes, time_graph, t_launch, args.eager)}
 
     cpu = None
     if not args.no_cpu_baseline:

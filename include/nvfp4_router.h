@@ -145,6 +145,18 @@ int router_forward(const void* x, int64_t T, int64_t D, const float* gsa_overrid
 /* Static text for a status code. */
 const char* router_status_string(int status);
 
+/*
+ * Measurement aid, not part of the router path: reads `bytes` of `buf`
+ * (device, 16-byte aligned, bytes % 16 == 0) once with 16-byte loads in one
+ * launch of min(bytes / 4096 rounded up, sink_words, 8192) workgroups of 256
+ * threads, and stores one XOR of the data per workgroup into `sink` (device,
+ * sink_words >= 1 words). Its duration is the time a kernel needs just to
+ * read that footprint, against which the gate kernels' rates are read
+ * (HBM bandwidth at a gigabyte; launch and cache latency at the decode
+ * gate's megabyte). Returns ROUTER_EINVAL for bad arguments.
+ */
+int router_probe_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,51 @@
+// Streaming-read probe: the time one launch needs to read a buffer once,
+// with 16-byte loads spread over as many workgroups as the buffer allows.
+// It measures the bandwidth a kernel can reach for a given footprint (HBM at
+// a gigabyte, launch and cache latency at the decode gate's megabyte), the
+// denominator against which the gate kernels' own rates are read. Not part
+// of the router path.
+#include "../../include/nvfp4_router.h"
+#include "router_internal.hpp"
+
+namespace nvr {
+
+constexpr int kProbeThreads = 256;
+constexpr int kProbeMaxGrid = 8192;
+
+__global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t* __restrict__ p, int64_t nvec,
+                                                                   uint32_t* __restrict__ sink) {
+  __shared__ uint32_t red[kProbeThreads / 64];
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
+  int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < nvec; i += stride) {
+    const u32x4_t v = p[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+}  // namespace nvr
+
+extern "C" int router_probe_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
+  if (!buf || !sink || sink_words == 0 || bytes == 0 || bytes % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(buf) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return ROUTER_EINVAL;
+  const int64_t nvec = (int64_t)(bytes / 16);
+  int64_t grid = (nvec + nvr::kProbeThreads - 1) / nvr::kProbeThreads;
+  if (grid > (int64_t)sink_words) grid = (int64_t)sink_words;
+  if (grid > nvr::kProbeMaxGrid) grid = nvr::kProbeMaxGrid;
+  nvr::probe_read_kernel<<<(int)grid, nvr::kProbeThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const nvr::u32x4_t*>(buf), nvec, sink);
+  return hipGetLastError() == hipSuccess ? ROUTER_OK : ROUTER_EHIP;
+}

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4_router.so")
 
 ROUTER_OK = 0
 EXPORTS = ("router_workspace_bytes", "router_workspace_init", "router_quantize", "router_gate_topk",
-           "router_forward", "router_status_string")
+           "router_forward", "router_status_string", "router_probe_read")
 
 _lib = None
 
@@ -48,6 +48,8 @@ def load_library(path=LIB_PATH):
     L.router_forward.restype = ctypes.c_int
     L.router_status_string.argtypes = [ctypes.c_int]
     L.router_status_string.restype = ctypes.c_char_p
+    L.router_probe_read.argtypes = [vp, sz, vp, sz, vp]
+    L.router_probe_read.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -185,3 +187,13 @@ def forward(x, wq, bias, k, routed_scale, workspace, gsa_override=None, want_log
                                          _ptr(bias), float(routed_scale), E, k, _ptr(idx), _ptr(w), _ptr(logits),
                                          _ptr(workspace.buf), workspace.nbytes, _stream()))
     return xq, out
+
+
+def probe_read(buf, sink):
+    """One streaming read of the whole of `buf` (a contiguous device tensor) by
+    the library's probe kernel, one XOR per workgroup into `sink` (int32 device
+    tensor); a measurement aid, not part of the router path."""
+    if not (buf.is_cuda and sink.is_cuda and buf.is_contiguous() and sink.dtype == torch.int32):
+        raise RouterError("probe_read: contiguous device buffer and int32 device sink required")
+    nbytes = buf.numel() * buf.element_size()
+    _check(load_library().router_probe_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(), _stream()))

@@ -89,3 +89,13 @@ def test_gate_rejects_bad_arguments(lib):
     assert call(xc=ctypes.c_void_p((1 << 20) + 4)) == -1
     assert call(work=None, nbytes=0) == -1  # split gate needs its counters
     assert call(nbytes=100) == -1
+
+
+def test_probe_rejects_bad_arguments(lib):
+    buf, sink = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)
+    assert lib.router_probe_read(None, 4096, sink, 16, None) == -1
+    assert lib.router_probe_read(buf, 4096, None, 16, None) == -1
+    assert lib.router_probe_read(buf, 4096, sink, 0, None) == -1
+    assert lib.router_probe_read(buf, 4100, sink, 16, None) == -1  # not a multiple of 16 bytes
+    assert lib.router_probe_read(ctypes.c_void_p(0x10008), 4096, sink, 16, None) == -1  # misaligned
+    assert lib.router_probe_read(buf, 0, sink, 16, None) == -1
