@@ -9,9 +9,9 @@
 //
 // Two kernels here, by token count T (T <= 4 takes the decode GEMV in
 // gate_decode.hip):
-//  * tile (T <= 256): 16x16 output tiles on 16x16x32 f16 MFMAs, the four
-//    waves of a workgroup splitting K and summing through LDS; the last
-//    workgroup of each 16-row tile routes it.
+//  * tile (T <= 256): 16x16 output tiles on 16x16x32 f16 MFMAs, the
+//    sixteen waves of a workgroup splitting K and summing through LDS; the
+//    last workgroup of each 16-row tile routes it.
 //  * mfma (larger T): BM tokens x 128 NTW experts per workgroup on 32x32x16
 //    f16 MFMAs; the accumulators go through LDS straight into the epilogue.
 //
@@ -55,53 +55,70 @@ struct TileArgs {
   int nsteps;  // 128-element K steps
 };
 
+// Sixteen wavefronts split a tile's K range, so each has only a few steps,
+// and issue the loads of up to four steps before their first MFMA; eight of
+// them route the tile's rows at the end.
+constexpr int kTileWaves = 16;
+constexpr int kTileThreads = 64 * kTileWaves;
+constexpr int kTileBatch = 4;   // K steps whose loads are in flight together
+constexpr int kTileRouters = 8;
+
 template <int JMAX>
-__global__ __launch_bounds__(256) void gate_tile_kernel(TileArgs a) {
-  __shared__ float part[4][16][17];
+__global__ __launch_bounds__(kTileThreads) void gate_tile_kernel(TileArgs a) {
+  __shared__ float part[kTileWaves][16][17];
   __shared__ float bias_s[512];
-  __shared__ WaveRouteScratch<JMAX> rsc[4];
+  __shared__ WaveRouteScratch<JMAX> rsc[kTileRouters];
   __shared__ uint32_t s_last;
   extern __shared__ float lg[];  // [16][E]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float bias0 = (int)threadIdx.x < a.E ? a.bias[threadIdx.x] : 0.0f;
-  const float bias1 = (int)threadIdx.x + 256 < a.E ? a.bias[threadIdx.x + 256] : 0.0f;
+  const float gsa = load_early(a.gsa), gsw = load_early(a.gsw);
   const int n = lane & 15, g = lane >> 4;
   const int col0 = blockIdx.x * 16, row0 = blockIdx.y * 16;
   const int arow = row0 + n, e = col0 + n;
   const bool a_ok = arow < a.T, b_ok = e < a.E;
-  const int s0 = a.nsteps * wave / 4, s1 = a.nsteps * (wave + 1) / 4;
+  const int s0 = a.nsteps * wave / kTileWaves, s1 = a.nsteps * (wave + 1) / kTileWaves;
 
+  // Chunks past this wavefront's steps or past D load as zeros and add
+  // nothing.
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  Chunk32 an = {}, bn = {};
-  if (s0 < s1) {
-    const int64_t k0 = (int64_t)s0 * 128 + 32 * g;
-    an = load_chunk(a.xc, a.xs, arow, a.D, k0, a_ok && k0 < a.D);
-    bn = load_chunk(a.wc, a.ws, e, a.D, k0, b_ok && k0 < a.D);
-  }
-  for (int s = s0; s < s1; ++s) {
-    const Chunk32 ac = an, bc = bn;
-    if (s + 1 < s1) {
-      const int64_t k0 = (int64_t)(s + 1) * 128 + 32 * g;
-      an = load_chunk(a.xc, a.xs, arow, a.D, k0, a_ok && k0 < a.D);
-      bn = load_chunk(a.wc, a.ws, e, a.D, k0, b_ok && k0 < a.D);
+  for (int sb = s0; sb < s1; sb += kTileBatch) {
+    Chunk32 ac[kTileBatch], bc[kTileBatch];
+#pragma unroll
+    for (int u = 0; u < kTileBatch; ++u) {
+      const int64_t k0 = (int64_t)(sb + u) * 128 + 32 * g;
+      const bool ok = sb + u < s1 && k0 < a.D;
+      ac[u] = load_chunk(a.xc, a.xs, arow, a.D, k0, a_ok && ok);
+      bc[u] = load_chunk(a.wc, a.ws, e, a.D, k0, b_ok && ok);
     }
-    const _Float16 sa0 = e4m3_f16(ac.s & 0xFFu), sa1 = e4m3_f16(ac.s >> 8);
-    const _Float16 sb0 = e4m3_f16(bc.s & 0xFFu), sb1 = e4m3_f16(bc.s >> 8);
-    acc = mfma16(fp4x8_to_f16(ac.c[0], sa0), fp4x8_to_f16(bc.c[0], sb0), acc);
-    acc = mfma16(fp4x8_to_f16(ac.c[1], sa0), fp4x8_to_f16(bc.c[1], sb0), acc);
-    acc = mfma16(fp4x8_to_f16(ac.c[2], sa1), fp4x8_to_f16(bc.c[2], sb1), acc);
-    acc = mfma16(fp4x8_to_f16(ac.c[3], sa1), fp4x8_to_f16(bc.c[3], sb1), acc);
+#pragma unroll
+    for (int u = 0; u < kTileBatch; ++u) {
+      const _Float16 sa0 = e4m3_f16(ac[u].s & 0xFFu), sa1 = e4m3_f16(ac[u].s >> 8);
+      const _Float16 sb0 = e4m3_f16(bc[u].s & 0xFFu), sb1 = e4m3_f16(bc[u].s >> 8);
+      acc = mfma16(fp4x8_to_f16(ac[u].c[0], sa0), fp4x8_to_f16(bc[u].c[0], sb0), acc);
+      acc = mfma16(fp4x8_to_f16(ac[u].c[1], sa0), fp4x8_to_f16(bc[u].c[1], sb0), acc);
+      acc = mfma16(fp4x8_to_f16(ac[u].c[2], sa1), fp4x8_to_f16(bc[u].c[2], sb1), acc);
+      acc = mfma16(fp4x8_to_f16(ac[u].c[3], sa1), fp4x8_to_f16(bc[u].c[3], sb1), acc);
+    }
   }
-  // 16x16 accumulator layout: lane holds rows 4g..4g+3 of column n.
+  // 16x16 accumulator layout: lane holds rows 4g..4g+3 of column n. The
+  // sixteen partial sums are added as a fixed pairwise tree.
 #pragma unroll
   for (int v = 0; v < 4; ++v) part[wave][4 * g + v][n] = acc[v];
   __syncthreads();
   if (wave == 0) {
-    const float scale = (*a.gsa) * (*a.gsw);
+    const float scale = gsa * gsw;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int m = 4 * g + v, r = row0 + m;
-      const float L = ((part[0][m][n] + part[1][m][n]) + (part[2][m][n] + part[3][m][n])) * scale;
+      float q[kTileWaves];
+#pragma unroll
+      for (int w = 0; w < kTileWaves; ++w) q[w] = part[w][m][n];
+#pragma unroll
+      for (int h = kTileWaves / 2; h >= 1; h >>= 1)
+#pragma unroll
+        for (int w = 0; w < h; ++w) q[w] = q[w] + q[w + h];
+      const float L = q[0] * scale;
       if (r < a.T && b_ok) {
         store_coherent(a.lbuf + (int64_t)r * a.E + e, L);
         if (a.logits_out) a.logits_out[(int64_t)r * a.E + e] = L;
@@ -110,14 +127,16 @@ __global__ __launch_bounds__(256) void gate_tile_kernel(TileArgs a) {
   }
   if (!arrive_last(&a.counters[blockIdx.y], gridDim.x, &s_last)) return;
   const int nrows = min(16, a.T - row0);
-  for (int i = threadIdx.x; i < nrows * a.E; i += 256) lg[i] = load_coherent(a.lbuf + (int64_t)row0 * a.E + i);
+  for (int i = threadIdx.x; i < nrows * a.E; i += kTileThreads)
+    lg[i] = load_coherent(a.lbuf + (int64_t)row0 * a.E + i);
   if ((int)threadIdx.x < a.E) bias_s[threadIdx.x] = bias0;
-  if ((int)threadIdx.x + 256 < a.E) bias_s[threadIdx.x + 256] = bias1;
   __syncthreads();
-  for (int m = wave; m < nrows; m += 4) {
-    const int64_t t = row0 + m;
-    wave_route_row<JMAX>(lg + m * a.E, bias_s, a.E, a.k, a.routed_scale, a.idx + t * a.k, a.w + t * a.k,
-                         rsc[wave]);
+  if (wave < kTileRouters) {
+    for (int m = wave; m < nrows; m += kTileRouters) {
+      const int64_t t = row0 + m;
+      wave_route_row<JMAX>(lg + m * a.E, bias_s, a.E, a.k, a.routed_scale, a.idx + t * a.k, a.w + t * a.k,
+                           rsc[wave]);
+    }
   }
   release_counter(&a.counters[blockIdx.y]);
 }
@@ -579,11 +598,11 @@ static hipError_t launch_tile(const TileArgs& a, hipStream_t stream) {
   const dim3 grid((a.E + 15) / 16, (a.T + 15) / 16);
   const size_t lds = (size_t)16 * a.E * sizeof(float);
   const int j = (a.E + 63) / 64;
-  if (j <= 1) gate_tile_kernel<1><<<grid, 256, lds, stream>>>(a);
-  else if (j <= 2) gate_tile_kernel<2><<<grid, 256, lds, stream>>>(a);
-  else if (j <= 4) gate_tile_kernel<4><<<grid, 256, lds, stream>>>(a);
-  else if (j <= 6) gate_tile_kernel<6><<<grid, 256, lds, stream>>>(a);
-  else gate_tile_kernel<8><<<grid, 256, lds, stream>>>(a);
+  if (j <= 1) gate_tile_kernel<1><<<grid, kTileThreads, lds, stream>>>(a);
+  else if (j <= 2) gate_tile_kernel<2><<<grid, kTileThreads, lds, stream>>>(a);
+  else if (j <= 4) gate_tile_kernel<4><<<grid, kTileThreads, lds, stream>>>(a);
+  else if (j <= 6) gate_tile_kernel<6><<<grid, kTileThreads, lds, stream>>>(a);
+  else gate_tile_kernel<8><<<grid, kTileThreads, lds, stream>>>(a);
   return hipGetLastError();
 }
 

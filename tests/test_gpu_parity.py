@@ -35,7 +35,9 @@ def dev():
 
 @pytest.fixture(scope="module")
 def ws(dev):
-    return rt.Workspace(WS_BYTES, dev)
+    # Large enough for every workload's call (the library sizes its own needs).
+    need = max(rt.workspace_bytes(c.T, c.D, c.E, c.k) for c in wl.CONFIGS.values())
+    return rt.Workspace(max(WS_BYTES, need), dev)
 
 
 def to_dev(bits, dev):
