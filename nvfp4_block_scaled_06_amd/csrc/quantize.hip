@@ -47,6 +47,25 @@ __device__ __forceinline__ uint32_t block_absmax(const uint32_t* w) {
   return m;
 }
 
+// The quantizer's common case: gsa in [2^-80, 2^100] (every tensor whose
+// magnitude is not extreme), decided once per launch. The block scale and
+// the codes then take block_scale's and encode8's fast path with no
+// double-precision fallback in the loop (a per-block choice would have the
+// compiler evaluate the fallback's division for every block). rcp6 is
+// rcp(6 gsa), hoisted out of the loop.
+__device__ __forceinline__ bool gsa_fast(float gsa) { return gsa >= 0x1p-80f && gsa <= 0x1p100f; }
+
+__device__ __forceinline__ void quant_block16_fast(const uint32_t* w, float gsa, float rcp6, uint32_t& c0,
+                                                   uint32_t& c1, uint32_t& sbyte) {
+  const float bmax = __uint_as_float(bf16_block_absmax(w) << 16);
+  const float p = bmax * rcp6;
+  sbyte = near_scale_key(p) < kNearScaleLimit ? e4m3_byte_exact(bmax, p, gsa) : e4m3_from_f32(fminf(p, 448.0f));
+  const float S = e4m3_value(sbyte);
+  const float inv = S > 0.0f ? __builtin_amdgcn_rcpf(gsa * S) : 0.0f;
+  c0 = fp4_exact8(w, inv, S, gsa);
+  c1 = fp4_exact8(w + 4, inv, S, gsa);
+}
+
 // Workgroup-wide max of a per-thread value (blockDim.x threads, multiple of 64).
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
   v = wave_max_u32(v);
@@ -81,12 +100,15 @@ __global__ __launch_bounds__(kSingleThreads) void quant_single_kernel(const u32x
     gsa = gsa_from_absmax_bits(block_max_u32(m, red));
   }
   if (threadIdx.x == 0) *gsa_out = gsa;
+  const bool fast = gsa_fast(gsa);
+  const float rcp6 = __builtin_amdgcn_rcpf(6.0f * gsa);
 #pragma unroll
   for (int j = 0; j < kSingleBlocksPerThread; ++j) {
     const int64_t b = threadIdx.x + (int64_t)j * kSingleThreads;
     if (b < nblocks) {
       uint32_t c0, c1, s;
-      quant_block16(w[j], gsa, c0, c1, s);
+      if (fast) quant_block16_fast(w[j], gsa, rcp6, c0, c1, s);
+      else quant_block16(w[j], gsa, c0, c1, s);
       codes[b] = make_uint2(c0, c1);
       scales[b] = (uint8_t)s;
     }
@@ -147,13 +169,26 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const u32x4_t* __r
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) *gsa_out = gsa;
   const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; b < nblocks; b += stride) {
-    uint32_t w[8];
-    load_block(x, b, w);
-    uint32_t c0, c1, s;
-    quant_block16(w, gsa, c0, c1, s);
-    codes[b] = make_uint2(c0, c1);
-    scales[b] = (uint8_t)s;
+  const int64_t b0 = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  if (gsa_fast(gsa)) {  // uniform
+    const float rcp6 = __builtin_amdgcn_rcpf(6.0f * gsa);
+    for (int64_t b = b0; b < nblocks; b += stride) {
+      uint32_t w[8];
+      load_block(x, b, w);
+      uint32_t c0, c1, s;
+      quant_block16_fast(w, gsa, rcp6, c0, c1, s);
+      codes[b] = make_uint2(c0, c1);
+      scales[b] = (uint8_t)s;
+    }
+  } else {
+    for (int64_t b = b0; b < nblocks; b += stride) {
+      uint32_t w[8];
+      load_block(x, b, w);
+      uint32_t c0, c1, s;
+      quant_block16(w, gsa, c0, c1, s);
+      codes[b] = make_uint2(c0, c1);
+      scales[b] = (uint8_t)s;
+    }
   }
 }
 

@@ -253,6 +253,8 @@ def synth(shape, seed, scale=1.0):
     (300, 2048, 384, 8),   # MFMA gate, 3 expert tiles per wave
     (65, 4096, 100, 6),    # E not a multiple of 32 (tile gate at this T)
     (96, 8192, 64, 4),
+    (33, 1056, 64, 4),     # tile gate: D not a multiple of 128, ragged row tile
+    (200, 160, 48, 5),     # tile gate: fewer K steps than wavefronts
     (600, 1056, 100, 6),   # MFMA gate: D not a multiple of 128, E not a multiple of 32
     (640, 384, 200, 8),    # MFMA gate, experts split over workgroups, second block partly empty
     (512, 512, 512, 32),   # MFMA gate, largest E and k
