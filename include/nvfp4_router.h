@@ -33,6 +33,13 @@
  *     other outputs unspecified.
  *   - Calls that share one workspace must not overlap in time (enqueue them
  *     on one stream).
+ *   - Tuning overrides, read once per process from the environment (results
+ *     stay within the stated tolerances for any accepted value; invalid
+ *     values are ignored): NVR_SPLIT_MAX_T (largest T on the 16x16-tile
+ *     gate, default 256), NVR_MMA_BM (prefill tokens per workgroup: 32, 64
+ *     or 128) with NVR_MMA_NTW (32-expert tiles per wavefront, 1..4). The
+ *     workspace size follows the same settings, so set them before the first
+ *     call and leave them.
  */
 #ifndef NVFP4_ROUTER_H
 #define NVFP4_ROUTER_H
