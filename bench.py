@@ -198,6 +198,69 @@ def probe_rates(torch, rt, c, nbytes, time_graph, t_launch, eager):
             "frac_of_achievable": t_small / t_launch, "hbm_1gib_gbs": (1 << 30) / t_big / 1e9}
 
 
+def lmhead_bench(torch, K, W, T=1, D=7168, N=129280):
+    """Greedy NVFP4 lm_head (lmhead_argmax) over an N x D vocabulary matrix: K calls graph-replayed after W
+    warm-ups, each streaming the packed weights (N D 9/16 bytes; 521 MB at the default size, twice the
+    Infinity Cache, so every call reads HBM). Prints one JSON line with the HBM roofline."""
+    from nvfp4_block_scaled_06_amd import router as rt
+
+    rt.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ws = rt.Workspace(max(rt.lmhead_workspace_bytes(T, D, N), rt.workspace_bytes(N, D, 1, 1)), dev)
+    g = torch.Generator(device=dev).manual_seed(1234)
+    w = (torch.randn((N, D), generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    wq = rt.quantize(w, ws)
+    del w
+    xs = [rt.quantize((torch.randn((T, D), generator=g, device=dev)).to(torch.bfloat16), ws) for _ in range(8)]
+    torch.cuda.synchronize()
+    for i in range(W):
+        rt.lmhead_argmax(xs[i % 8], wq, ws)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(gr, stream=st):
+            for i in range(K):
+                rt.lmhead_argmax(xs[i % 8], wq, ws)
+    torch.cuda.current_stream().wait_stream(st)
+    gr.replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    gr.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / K
+    nbytes = N * D * 9 // 16 + T * D * 9 // 16 + 8 + 8 * T
+    big = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(8192, dtype=torch.int32, device=dev)
+    rt.probe_read(big, sink)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in ev:
+        a.record(cur)
+        rt.probe_read(big, sink)
+        b.record(cur)
+    torch.cuda.synchronize()
+    probe = (1 << 30) / (float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3) / 1e9
+    achieved = nbytes / t / 1e9
+    log(f"lm_head N={N} D={D} T={T}: {t * 1e6:.1f} us per call, {achieved:.0f} GB/s; read probe {probe:.0f} GB/s")
+    print(json.dumps({
+        "metric": f"greedy NVFP4 lm_head GEMV+argmax calls/s, N={N} D={D} T={T}", "value": 1.0 / t, "unit": "calls/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": t * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "nvfp4 operands, f16 products, f32 accumulate", "data": "synthetic",
+        "config": {"workload": f"lm_head decode T={T} D={D} N={N}", "entry": "lmhead_argmax", "launch": "hipgraph",
+                   "us_per_call": t * 1e6},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "lmhead_argmax_kernel",
+                     "algorithmic": f"{nbytes} B per launch", "read_probe_1gib_gbs": probe,
+                     "frac_of_read_probe": achieved / probe},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,6 +270,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lmhead", action="store_true",
+                    help="time the greedy NVFP4 lm_head (129280 x 7168, T=1) instead of the router")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="time a plain device copy of this many MiB instead of the router")
     args = ap.parse_args()
@@ -219,6 +284,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration, max(args.steps, 1))
+        return
+    if args.lmhead:
+        lmhead_bench(torch, min(args.steps, 200), min(args.warmup, 20))
         return
 
     from nvfp4_block_scaled_06_amd import router as rt

@@ -153,6 +153,36 @@ int router_forward(const void* x, int64_t T, int64_t D, const float* gsa_overrid
 const char* router_status_string(int status);
 
 /*
+ * lm_head-shaped NVFP4 GEMV with a greedy (top-1) epilogue: for each of T
+ * tokens, logits[t, n] = gsa * gsw * sum_d xhat[t, d] * what[n, d] (fp32
+ * accumulation, the same arithmetic as the router's gate) over an N-row
+ * vocabulary matrix, and the row with the largest logit (an exact tie going
+ * to the lower row). The NVFP4 lm_head replaces a 1.8 GB BF16 weight (commit
+ * df05289d, dsv4/layers/grouped_linear.py, weights paragraph); at decode
+ * size the call streams the packed weights once.
+ *
+ *   x_codes, x_scales, gsa   router_quantize outputs for x [T, D] (16- and
+ *                            2-byte aligned).
+ *   w_codes, w_scales, gsw   the weights in the same format: [N, D/2],
+ *                            [N, D/16] (16- and 2-byte aligned) and a device
+ *                            fp32 scalar.
+ *   T, D, N                  0 <= T <= 4; 32 <= D <= 16384, D % 32 == 0;
+ *                            T * D <= 32768; 1 <= N <= 2^30.
+ *   out_idx, out_logit       [T] int32 / fp32 out: the chosen row and its
+ *                            logit.
+ *   logits_out               NULL, or [T, N] fp32 out: every logit.
+ *   workspace                256-byte aligned, lmhead_workspace_bytes(T, D,
+ *                            N) bytes; its first 4096 bytes are the arrival
+ *                            counters shared with the router calls (zero
+ *                            between calls, see router_workspace_bytes).
+ * Returns ROUTER_EINVAL for bad shapes, pointers or workspace.
+ */
+size_t lmhead_workspace_bytes(int64_t T, int64_t D, int64_t N);
+int lmhead_argmax(const uint8_t* x_codes, const uint8_t* x_scales, const float* gsa, const uint8_t* w_codes,
+                  const uint8_t* w_scales, const float* gsw, int64_t T, int64_t D, int64_t N, int32_t* out_idx,
+                  float* out_logit, float* logits_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Measurement aid, not part of the router path: reads `bytes` of `buf`
  * (device, 16-byte aligned, bytes % 16 == 0) once with 16-byte loads in one
  * launch of min(bytes / 4096 rounded up, sink_words, 8192) workgroups of 256

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4_router.so")
 
 ROUTER_OK = 0
 EXPORTS = ("router_workspace_bytes", "router_workspace_init", "router_quantize", "router_gate_topk",
-           "router_forward", "router_status_string", "router_probe_read")
+           "router_forward", "router_status_string", "router_probe_read", "lmhead_workspace_bytes",
+           "lmhead_argmax")
 
 _lib = None
 
@@ -50,6 +51,10 @@ def load_library(path=LIB_PATH):
     L.router_status_string.restype = ctypes.c_char_p
     L.router_probe_read.argtypes = [vp, sz, vp, sz, vp]
     L.router_probe_read.restype = ctypes.c_int
+    L.lmhead_workspace_bytes.argtypes = [i64, i64, i64]
+    L.lmhead_workspace_bytes.restype = sz
+    L.lmhead_argmax.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    L.lmhead_argmax.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -197,3 +202,26 @@ def probe_read(buf, sink):
         raise RouterError("probe_read: contiguous device buffer and int32 device sink required")
     nbytes = buf.numel() * buf.element_size()
     _check(load_library().router_probe_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(), _stream()))
+
+
+def lmhead_workspace_bytes(T, D, N):
+    n = load_library().lmhead_workspace_bytes(T, D, N)
+    if n == 0:
+        raise RouterError(f"invalid lm_head sizes T={T} D={D} N={N}")
+    return n
+
+
+def lmhead_argmax(xq, wq, workspace, want_logits=False):
+    """Greedy lm_head over NVFP4 x [T, D] and weights [N, D]: returns ``(idx [T] int32, logit [T] fp32, logits
+    [T, N] fp32 or None)``."""
+    T, D, N = xq.rows, xq.D, wq.rows
+    if wq.D != D:
+        raise RouterError("lm_head weights do not match x")
+    dev = xq.codes.device
+    idx = torch.empty(T, dtype=torch.int32, device=dev)
+    logit = torch.empty(T, dtype=torch.float32, device=dev)
+    logits = torch.empty((T, N), dtype=torch.float32, device=dev) if want_logits else None
+    _check(load_library().lmhead_argmax(_ptr(xq.codes), _ptr(xq.scales), _ptr(xq.gscale), _ptr(wq.codes),
+                                        _ptr(wq.scales), _ptr(wq.gscale), T, D, N, _ptr(idx), _ptr(logit),
+                                        _ptr(logits), _ptr(workspace.buf), workspace.nbytes, _stream()))
+    return idx, logit, logits

@@ -32,6 +32,8 @@ Parity status per function:
 * ``router_ref``: pinned (hand cases, zero-input and zero-bias reductions,
   brute-force subsets, exact-rational logits).
 * ``check``: pinned by mutation tests (planted mistakes must be caught).
+* ``lmhead_ref``: pinned (one-hot hand case with a tie, brute force over
+  rows, mutation tests of its checker); its logits are router_ref's.
 
 Two conventions are not fixed by the pages and are parity unpinned by them:
 the nibble order of packed codes (even element in the low nibble) and the
@@ -39,4 +41,4 @@ code of -0 and of negatives that round to zero (sign kept: 0x8). The tests
 pin the oracle to these stated conventions.
 """
 
-from . import formats, quant_ref, router_ref, check  # noqa: F401
+from . import formats, quant_ref, router_ref, check, lmhead_ref  # noqa: F401

@@ -99,3 +99,23 @@ def test_probe_rejects_bad_arguments(lib):
     assert lib.router_probe_read(buf, 4100, sink, 16, None) == -1  # not a multiple of 16 bytes
     assert lib.router_probe_read(ctypes.c_void_p(0x10008), 4096, sink, 16, None) == -1  # misaligned
     assert lib.router_probe_read(buf, 0, sink, 16, None) == -1
+
+
+def test_lmhead_workspace_and_validation(lib):
+    # counters + one 8-byte candidate per token and 64-row workgroup
+    assert lib.lmhead_workspace_bytes(1, 7168, 129280) == 4096 + 8 * 2020
+    assert lib.lmhead_workspace_bytes(4, 7168, 65) == 4096 + 8 * 4 * 2
+    for bad in [(5, 7168, 10), (1, 7160, 10), (1, 16416, 10), (1, 7168, 0), (-1, 7168, 10), (4, 16384, 10)]:
+        assert lib.lmhead_workspace_bytes(*bad) == 0, bad
+    p = ctypes.c_void_p(0x100000)
+    args = [p, p, p, p, p, p, 1, 7168, 100, p, p, None, p, 1 << 20, None]
+    bad_d = list(args); bad_d[7] = 7160
+    assert lib.lmhead_argmax(*bad_d) == -1
+    no_ws = list(args); no_ws[12] = None
+    assert lib.lmhead_argmax(*no_ws) == -1
+    small_ws = list(args); small_ws[13] = 100
+    assert lib.lmhead_argmax(*small_ws) == -1
+    odd = list(args); odd[0] = ctypes.c_void_p(0x100008)  # x codes not 16-byte aligned
+    assert lib.lmhead_argmax(*odd) == -1
+    empty = list(args); empty[6] = 0
+    assert lib.lmhead_argmax(*empty) == 0  # T == 0: nothing to do
