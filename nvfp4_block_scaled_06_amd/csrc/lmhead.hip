@@ -12,6 +12,9 @@
 //  * Workgroup: 64 rows, four wavefronts of 16 rows, 4 rows in flight per
 //    wavefront; lane l takes the 32-element chunks l, l + 64, ... of a row
 //    (16 code bytes and 2 scale bytes each, coalesced 1 KB per wavefront).
+//    The weights are read once per call, with nontemporal loads (measured:
+//    110 us against 115 us with cached loads at 129,280 x 7168; 8 rows in
+//    flight or 8 rows per wavefront were no faster).
 //  * x: the tokens' chunks are converted once per workgroup into LDS as
 //    exact fp16 q S values, the weight chunks in registers; block products
 //    are exact in fp32 and the per-lane sums and the wavefront sum run in a
@@ -107,9 +110,10 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_argmax_kernel(LmArgs a) {
       for (int i = 0; i < CPL; ++i) {
         const int c = lane + 64 * i;
         const bool ok = row < a.N && c < nch;
-        wv[u][i] = ok ? *reinterpret_cast<const u32x4_t*>(a.wc + (int64_t)row * rowc + 16 * c)
-                      : u32x4_t{0u, 0u, 0u, 0u};
-        wsv[u][i] = ok ? *reinterpret_cast<const uint16_t*>(a.ws + (int64_t)row * rows + 2 * c) : 0u;
+        const u32x4_t* pc = reinterpret_cast<const u32x4_t*>(a.wc + (int64_t)row * rowc + 16 * c);
+        const uint16_t* ps = reinterpret_cast<const uint16_t*>(a.ws + (int64_t)row * rows + 2 * c);
+        wv[u][i] = ok ? __builtin_nontemporal_load(pc) : u32x4_t{0u, 0u, 0u, 0u};
+        wsv[u][i] = ok ? __builtin_nontemporal_load(ps) : 0u;
       }
     }
 #pragma unroll
