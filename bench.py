@@ -191,11 +191,17 @@ def probe_rates(torch, rt, c, nbytes, time_graph, t_launch, eager):
         b.record(cur)
     torch.cuda.synchronize()
     t_big = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    # One buffer read over and over (hot in L2), replayed like the router: the latency floor of such a read.
+    t_one = None
+    if not eager:
+        _, ev_one = time_graph(lambda i: rt.probe_read(bufs[0], sink))
+        t_one = ev_one / time_graph.steps
     del big, bufs
     log(f"probe: {fb} B in {t_small * 1e6:.2f} us per launch; 1 GiB at {(1 << 30) / t_big / 1e9:.0f} GB/s")
     return {"kernel": "probe_read_kernel", "footprint_bytes": fb, "buffers": c.layers,
             "launch_us": t_small * 1e6, "achievable_gbs": fb / t_small / 1e9,
-            "frac_of_achievable": t_small / t_launch, "hbm_1gib_gbs": (1 << 30) / t_big / 1e9}
+            "frac_of_achievable": t_small / t_launch, "hbm_1gib_gbs": (1 << 30) / t_big / 1e9,
+            "one_hot_buffer_launch_us": None if t_one is None else t_one * 1e6}
 
 
 def lmhead_bench(torch, K, W, T=1, D=7168, N=129280):
@@ -270,6 +276,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time router calls that each follow a 1 GiB read (weights no longer in the Infinity Cache)")
     ap.add_argument("--lmhead", action="store_true",
                     help="time the greedy NVFP4 lm_head (129280 x 7168, T=1) instead of the router")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
@@ -391,12 +399,18 @@ def main():
                                            out=out))
     log(f"launch times: forward {tf * 1e6:.2f} us, quantize {tq * 1e6:.2f} us, gate {tg * 1e6:.2f} us")
 
-    if c.T > 4:
+    if c.T > 256:
         achieved = gate_flops(c) / tg / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None,
-                "kernel": "gate_mfma_kernel" if c.T > 256 else "gate_tile_kernel",
+                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None, "kernel": "gate_mfma_kernel",
                 "algorithmic": f"{gate_flops(c)} FLOP per launch"}
+    elif c.T > 4:
+        # Batched decode: a few hundred MFLOP against a megabyte of weights; bytes bound it (in practice the
+        # loads' and the handoff's latency).
+        achieved = gate_bytes(c) / tg / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gate_tile_kernel",
+                "algorithmic": f"{gate_bytes(c)} B per launch"}
     else:
         # One launch per step: the events around the timed replay give the average launch duration.
         nbytes = forward_bytes(c)
@@ -409,6 +423,39 @@ def main():
                 "launch_us": t_launch * 1e6,
                 "algorithmic": f"{nbytes} B per launch",
                 "probe": probe_rates(torch, rt, c, nbytes, time_graph, t_launch, args.eager)}
+
+    cold = None
+    if args.cold:
+        # A 1 GiB streaming read before every call evicts the 256 MB Infinity Cache, so the call's weights
+        # come from HBM. Graphs of 100 (read, call) pairs and of 100 reads alone are replayed; the
+        # difference per pair is the cold call.
+        flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.empty(8192, dtype=torch.int32, device=dev)
+
+        def replay(with_call):
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    for i in range(100):
+                        rt.probe_read(flush, sink)
+                        if with_call:
+                            step_forward(W + i)
+            torch.cuda.current_stream().wait_stream(s)
+            g.replay()
+            torch.cuda.synchronize()
+            c = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(c)
+            g.replay()
+            e1.record(c)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e-3
+
+        cold = (replay(True) - replay(False)) / 100
+        del flush
+        log(f"cold (after a 1 GiB read): forward {cold * 1e6:.2f} us per call")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -440,6 +487,7 @@ def main():
             "forward_launch_us": tf * 1e6,
             "quantize_launch_us": tq * 1e6,
             "gate_launch_us": tg * 1e6,
+            **({"cold_forward_launch_us": cold * 1e6} if cold is not None else {}),
             "parallelism": "single GPU",
         },
         "roofline": roof,
