@@ -56,18 +56,23 @@ struct TileArgs {
 };
 
 // Sixteen wavefronts split a tile's K range, so each has only a few steps,
-// and issue the loads of up to four steps before their first MFMA; eight of
-// them route the tile's rows at the end.
+// and issue the loads of up to four steps before their first MFMA; at the
+// end each routes one of the tile's rows. The K partial sums and the router
+// scratch share LDS (the partials are dead once the tile's logits are out).
 constexpr int kTileWaves = 16;
 constexpr int kTileThreads = 64 * kTileWaves;
-constexpr int kTileBatch = 4;   // K steps whose loads are in flight together
-constexpr int kTileRouters = 8;
+constexpr int kTileBatch = 4;  // K steps whose loads are in flight together
+
+template <int JMAX>
+union TileLds {
+  float part[kTileWaves][16][17];
+  WaveRouteScratch<JMAX> rsc[kTileWaves];
+};
 
 template <int JMAX>
 __global__ __launch_bounds__(kTileThreads) void gate_tile_kernel(TileArgs a) {
-  __shared__ float part[kTileWaves][16][17];
+  __shared__ TileLds<JMAX> u;
   __shared__ float bias_s[512];
-  __shared__ WaveRouteScratch<JMAX> rsc[kTileRouters];
   __shared__ uint32_t s_last;
   extern __shared__ float lg[];  // [16][E]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -104,7 +109,7 @@ __global__ __launch_bounds__(kTileThreads) void gate_tile_kernel(TileArgs a) {
   // 16x16 accumulator layout: lane holds rows 4g..4g+3 of column n. The
   // sixteen partial sums are added as a fixed pairwise tree.
 #pragma unroll
-  for (int v = 0; v < 4; ++v) part[wave][4 * g + v][n] = acc[v];
+  for (int v = 0; v < 4; ++v) u.part[wave][4 * g + v][n] = acc[v];
   __syncthreads();
   if (wave == 0) {
     const float scale = gsa * gsw;
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(kTileThreads) void gate_tile_kernel(TileArgs a) {
       const int m = 4 * g + v, r = row0 + m;
       float q[kTileWaves];
 #pragma unroll
-      for (int w = 0; w < kTileWaves; ++w) q[w] = part[w][m][n];
+      for (int w = 0; w < kTileWaves; ++w) q[w] = u.part[w][m][n];
 #pragma unroll
       for (int h = kTileWaves / 2; h >= 1; h >>= 1)
 #pragma unroll
@@ -131,12 +136,10 @@ __global__ __launch_bounds__(kTileThreads) void gate_tile_kernel(TileArgs a) {
     lg[i] = load_coherent(a.lbuf + (int64_t)row0 * a.E + i);
   if ((int)threadIdx.x < a.E) bias_s[threadIdx.x] = bias0;
   __syncthreads();
-  if (wave < kTileRouters) {
-    for (int m = wave; m < nrows; m += kTileRouters) {
-      const int64_t t = row0 + m;
-      wave_route_row<JMAX>(lg + m * a.E, bias_s, a.E, a.k, a.routed_scale, a.idx + t * a.k, a.w + t * a.k,
-                           rsc[wave]);
-    }
+  if (wave < nrows) {  // 16 rows at most: one per wavefront
+    const int64_t t = row0 + wave;
+    wave_route_row<JMAX>(lg + wave * a.E, bias_s, a.E, a.k, a.routed_scale, a.idx + t * a.k, a.w + t * a.k,
+                         u.rsc[wave]);
   }
   release_counter(&a.counters[blockIdx.y]);
 }
