@@ -12,6 +12,18 @@ namespace nvr {
 constexpr int kProbeThreads = 256;
 constexpr int kProbeMaxGrid = 8192;
 
+// Buffers larger than the Infinity Cache are streamed with nontemporal loads
+// (the faster way to read HBM once); smaller ones with ordinary loads, which
+// the caches keep.
+constexpr int64_t kProbeStreamBytes = 256ll << 20;
+
+template <bool NT>
+__device__ __forceinline__ u32x4_t probe_load(const u32x4_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t* __restrict__ p, int64_t nvec,
                                                                    uint32_t* __restrict__ sink) {
   __shared__ uint32_t red[kProbeThreads / 64];
@@ -21,12 +33,12 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t
   for (; i + 3 * stride < nvec; i += 4 * stride) {
     u32x4_t v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = p[i + u * stride];
+    for (int u = 0; u < 4; ++u) v[u] = probe_load<NT>(p + i + u * stride);
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   for (; i < nvec; i += stride) {
-    const u32x4_t v = p[i];
+    const u32x4_t v = probe_load<NT>(p + i);
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
@@ -45,7 +57,11 @@ extern "C" int router_probe_read(const void* buf, size_t bytes, uint32_t* sink, 
   int64_t grid = (nvec + nvr::kProbeThreads - 1) / nvr::kProbeThreads;
   if (grid > (int64_t)sink_words) grid = (int64_t)sink_words;
   if (grid > nvr::kProbeMaxGrid) grid = nvr::kProbeMaxGrid;
-  nvr::probe_read_kernel<<<(int)grid, nvr::kProbeThreads, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const nvr::u32x4_t*>(buf), nvec, sink);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const nvr::u32x4_t* p = static_cast<const nvr::u32x4_t*>(buf);
+  if ((int64_t)bytes > nvr::kProbeStreamBytes)
+    nvr::probe_read_kernel<true><<<(int)grid, nvr::kProbeThreads, 0, s>>>(p, nvec, sink);
+  else
+    nvr::probe_read_kernel<false><<<(int)grid, nvr::kProbeThreads, 0, s>>>(p, nvec, sink);
   return hipGetLastError() == hipSuccess ? ROUTER_OK : ROUTER_EHIP;
 }
