@@ -91,9 +91,11 @@ __device__ __forceinline__ uint32_t sign_codes4(const uint32_t* w) {
 // hardware conversion (round to nearest even, saturating) then maps to the
 // right code. Every E2M1 value and every rounding threshold (0.25, 0.75,
 // 1.25, 1.75, 2.5, 3.5, 5) has at most two explicit mantissa bits:
-//  1. v = the value nearest qa with at most two explicit mantissa bits (qa
-//     clamped to 7 first: everything above 5 saturates to 6). Between v and
-//     q there is no threshold other than v itself.
+//  1. v = the value nearest qa with at most two explicit mantissa bits.
+//     Between v and q there is no threshold other than v itself. A huge qa
+//     (a too-small static gsa) may round to +inf; then v S gsa is +inf, the
+//     residual below is -inf, v moves down to a large finite value and the
+//     conversion saturates to 6, as q does.
 //  2. r = |x| - v S gsa by one fma has the exact sign of q - v: v S is exact
 //     (at most 7 significant bits) and every term is a multiple of
 //     2^-31 v S gsa, far above the fp32 underflow threshold in this range,
@@ -109,7 +111,7 @@ __device__ __forceinline__ uint32_t sign_codes4(const uint32_t* w) {
 // The sign is copied from x last, so -0 and tiny negatives keep their sign.
 __device__ __forceinline__ float e2m1_exact_input(float x, float inv, float S, float gsa) {
   const float xa = fabsf(x);
-  const float qa = fminf(xa * inv, 7.0f);
+  const float qa = xa * inv;
   const uint32_t vb = (__float_as_uint(qa) + 0x100000u) & 0xFFE00000u;
   const float r = fmaf(-(__uint_as_float(vb) * S), gsa, xa);
   // One v_med3_i32 (the compiler would otherwise lower the clamp to two

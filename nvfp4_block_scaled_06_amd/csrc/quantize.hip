@@ -222,8 +222,11 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t D, const float* 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
+  // Equal grid-stride passes for every thread: a last pass that only part of
+  // the threads take would cost the whole VALU issue of one.
   const int64_t want = (nblocks + kQuantThreads - 1) / kQuantThreads;
-  const int grid = (int)(want < kQuantMaxGrid ? want : kQuantMaxGrid);
+  const int64_t passes = (want + kQuantMaxGrid - 1) / kQuantMaxGrid;
+  const int grid = (int)((want + passes - 1) / passes);
   quant_kernel<<<grid, kQuantThreads, 0, stream>>>(xv, nblocks, partial, npartial, gsa_override, cv, scales,
                                                    gsa_out);
   return hipGetLastError();
