@@ -174,7 +174,7 @@ constexpr int kMmaThreads = 256;
 // accumulators and weight fragments of a wide tile already need most registers.
 template <int BM, int NTW>
 constexpr int mma_ring() {
-  return (BM / 32) * NTW >= 6 ? 3 : 4;
+  return (BM / 32) * NTW >= 6 ? 2 : 4;
 }
 constexpr int kMmaARow = 136;  // LDS row stride of the A tile in halves (128 values + 8 pad)
 
