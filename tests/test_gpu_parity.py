@@ -344,7 +344,9 @@ def test_graph_capture_replays_match_eager(dev, ws, cfg):
 
 
 @pytest.mark.parametrize("cfg,T,D,E,k", [(2, 1, 7168, 256, 8), (None, 3, 7168, 256, 8), (None, 4, 2048, 384, 8),
-                                         (None, 2, 16384, 64, 4), (None, 9, 7168, 256, 8), (1, 4, 256, 16, 2)])
+                                         (None, 2, 16384, 64, 4), (None, 9, 7168, 256, 8), (1, 4, 256, 16, 2),
+                                         (None, 4, 16384, 512, 32),  # single launch at its largest D, E and k
+                                         (None, 1, 16416, 100, 5)])  # D past the single launch: two-call path
 def test_forward_matches_oracle(dev, ws, cfg, T, D, E, k):
     """router_forward (single launch at decode sizes) gives the quantizer's bytes and the oracle's routing."""
     if cfg is not None:
