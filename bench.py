@@ -152,7 +152,7 @@ def copy_calibration(torch, mib, reps):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": reps}), flush=True)
 
 
-def probe_rates(torch, rt, c, nbytes, time_graph, t_launch, eager):
+def probe_rates(torch, rt, c, nbytes, time_graph, steps, t_launch, eager):
     """What a kernel that only reads can reach: the library's streaming-read probe over a footprint of the
     gate's algorithmic bytes, cycled over as many buffers as there are layer sets and replayed like the
     router (the achievable rate for this footprint), and over 1 GiB (the achievable HBM bandwidth)."""
@@ -179,7 +179,7 @@ def probe_rates(torch, rt, c, nbytes, time_graph, t_launch, eager):
         t_small = e0.elapsed_time(e1) * 1e-3 / 200
     else:
         _, ev = time_graph(step_probe)
-        t_small = ev / time_graph.steps
+        t_small = ev / steps
     big = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
     rt.probe_read(big, sink)
     torch.cuda.synchronize()
@@ -195,7 +195,7 @@ def probe_rates(torch, rt, c, nbytes, time_graph, t_launch, eager):
     t_one = None
     if not eager:
         _, ev_one = time_graph(lambda i: rt.probe_read(bufs[0], sink))
-        t_one = ev_one / time_graph.steps
+        t_one = ev_one / steps
     del big, bufs
     log(f"probe: {fb} B in {t_small * 1e6:.2f} us per launch; 1 GiB at {(1 << 30) / t_big / 1e9:.0f} GB/s")
     return {"kernel": "probe_read_kernel", "footprint_bytes": fb, "buffers": c.layers,
@@ -361,7 +361,6 @@ def main():
         del g
         return dt, e0.elapsed_time(e1) * 1e-3
 
-    time_graph.steps = K
 
     for step in (step_forward, step_two_calls):
         for i in range(W):
@@ -422,7 +421,7 @@ def main():
                 "kernel": "gate_decode_kernel (quantizing; the whole call is one launch)",
                 "launch_us": t_launch * 1e6,
                 "algorithmic": f"{nbytes} B per launch",
-                "probe": probe_rates(torch, rt, c, nbytes, time_graph, t_launch, args.eager)}
+                "probe": probe_rates(torch, rt, c, nbytes, time_graph, K, t_launch, args.eager)}
 
     cold = None
     if args.cold:
