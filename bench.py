@@ -204,6 +204,25 @@ def probe_rates(torch, rt, c, nbytes, time_graph, steps, t_launch, eager):
             "one_hot_buffer_launch_us": None if t_one is None else t_one * 1e6}
 
 
+def mfma_probe_tflops(torch, rt, iters=4000):
+    """fp16 MFMA rate the chip sustains at its running clock: the library's MFMA probe (four independent
+    32x32x16 chains per wavefront, four wavefronts per SIMD, no memory traffic), median of 5 launches."""
+    sink = torch.empty(rt.MFMA_PROBE_SINK, dtype=torch.float32, device="cuda:0")
+    rt.probe_mfma(iters, sink)
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for a, b in ev:
+        a.record(cur)
+        rt.probe_mfma(iters, sink)
+        b.record(cur)
+    torch.cuda.synchronize()
+    t = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    tflops = 1024 * 4 * iters * 4 * 32768 / t / 1e12
+    log(f"MFMA probe: {tflops:.0f} TFLOP/s fp16")
+    return tflops
+
+
 def lmhead_bench(torch, K, W, T=1, D=7168, N=129280):
     """Greedy NVFP4 lm_head (lmhead_argmax) over an N x D vocabulary matrix: K calls graph-replayed after W
     warm-ups, each streaming the packed weights (N D 9/16 bytes; 521 MB at the default size, twice the
@@ -400,9 +419,11 @@ def main():
 
     if c.T > 256:
         achieved = gate_flops(c) / tg / 1e12
+        probe = mfma_probe_tflops(torch, rt)
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None, "kernel": "gate_mfma_kernel",
-                "algorithmic": f"{gate_flops(c)} FLOP per launch"}
+                "algorithmic": f"{gate_flops(c)} FLOP per launch",
+                "mfma_probe_tflops": probe, "frac_of_mfma_probe": achieved / probe}
     elif c.T > 4:
         # Batched decode: a few hundred MFLOP against a megabyte of weights; bytes bound it (in practice the
         # loads' and the handoff's latency).

@@ -194,6 +194,17 @@ int lmhead_argmax(const uint8_t* x_codes, const uint8_t* x_scales, const float* 
  */
 int router_probe_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream);
 
+/*
+ * Measurement aid, not part of the router path: 1024 workgroups of 256
+ * threads (four wavefronts per SIMD on 256 compute units) each run `iters`
+ * rounds of four independent 32x32x16 fp16 MFMA chains with no memory
+ * traffic, then store one float per thread into `sink` (device, at least
+ * 262144 floats). Its duration gives the fp16 MFMA rate the chip sustains at
+ * its running clock: 1024 * 4 * iters * 4 * 32768 FLOP per launch. 1 <= iters
+ * <= 2^24; ROUTER_EINVAL otherwise.
+ */
+int router_probe_mfma(int64_t iters, float* sink, size_t sink_floats, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

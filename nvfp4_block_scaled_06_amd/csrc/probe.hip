@@ -47,7 +47,50 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t
   if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
+// MFMA probe: every wavefront runs `iters` rounds of four independent
+// 32x32x16 f16 MFMA chains (no memory traffic in the loop), then stores one
+// float per thread so the work is kept. Launched with four wavefronts per
+// SIMD on every compute unit, it measures the matrix-core rate the chip
+// sustains at its running clock.
+constexpr int kMfmaProbeGrid = 1024;  // workgroups of 256 threads: 4 per CU, one wavefront each per SIMD
+
+__global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(int iters, float* __restrict__ sink) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  typedef float f16x __attribute__((ext_vector_type(16)));
+  const int lane = threadIdx.x & 63;
+  h8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (_Float16)((lane + i) & 7) * (_Float16)0.125f;
+    b[i] = (_Float16)((lane * 3 + i) & 7) * (_Float16)0.0625f;
+  }
+  f16x acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) r += acc[j][v];
+  sink[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = r;
+}
+
 }  // namespace nvr
+
+extern "C" int router_probe_mfma(int64_t iters, float* sink, size_t sink_floats, void* stream) {
+  if (iters < 1 || iters > (int64_t(1) << 24) || !sink || reinterpret_cast<uintptr_t>(sink) % 4 != 0 ||
+      sink_floats < (size_t)nvr::kMfmaProbeGrid * nvr::kProbeThreads)
+    return ROUTER_EINVAL;
+  nvr::probe_mfma_kernel<<<nvr::kMfmaProbeGrid, nvr::kProbeThreads, 0, static_cast<hipStream_t>(stream)>>>((int)iters,
+                                                                                                          sink);
+  return hipGetLastError() == hipSuccess ? ROUTER_OK : ROUTER_EHIP;
+}
 
 extern "C" int router_probe_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
   if (!buf || !sink || sink_words == 0 || bytes == 0 || bytes % 16 != 0 ||

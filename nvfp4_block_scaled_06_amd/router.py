@@ -16,8 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4_router.so")
 
 ROUTER_OK = 0
 EXPORTS = ("router_workspace_bytes", "router_workspace_init", "router_quantize", "router_gate_topk",
-           "router_forward", "router_status_string", "router_probe_read", "lmhead_workspace_bytes",
-           "lmhead_argmax")
+           "router_forward", "router_status_string", "router_probe_read", "router_probe_mfma",
+           "lmhead_workspace_bytes", "lmhead_argmax")
 
 _lib = None
 
@@ -51,6 +51,8 @@ def load_library(path=LIB_PATH):
     L.router_status_string.restype = ctypes.c_char_p
     L.router_probe_read.argtypes = [vp, sz, vp, sz, vp]
     L.router_probe_read.restype = ctypes.c_int
+    L.router_probe_mfma.argtypes = [i64, vp, sz, vp]
+    L.router_probe_mfma.restype = ctypes.c_int
     L.lmhead_workspace_bytes.argtypes = [i64, i64, i64]
     L.lmhead_workspace_bytes.restype = sz
     L.lmhead_argmax.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
@@ -225,3 +227,13 @@ def lmhead_argmax(xq, wq, workspace, want_logits=False):
                                         _ptr(wq.scales), _ptr(wq.gscale), T, D, N, _ptr(idx), _ptr(logit),
                                         _ptr(logits), _ptr(workspace.buf), workspace.nbytes, _stream()))
     return idx, logit, logits
+
+
+MFMA_PROBE_SINK = 1024 * 256
+
+
+def probe_mfma(iters, sink):
+    """Back-to-back fp16 MFMAs on every SIMD (a measurement aid): 1024 * 4 * iters * 4 * 32768 FLOP."""
+    if not (sink.is_cuda and sink.dtype == torch.float32 and sink.numel() >= MFMA_PROBE_SINK):
+        raise RouterError("probe_mfma: fp32 device sink of at least 262144 floats required")
+    _check(load_library().router_probe_mfma(int(iters), _ptr(sink), sink.numel(), _stream()))

@@ -119,3 +119,11 @@ def test_lmhead_workspace_and_validation(lib):
     assert lib.lmhead_argmax(*odd) == -1
     empty = list(args); empty[6] = 0
     assert lib.lmhead_argmax(*empty) == 0  # T == 0: nothing to do
+
+
+def test_mfma_probe_rejects_bad_arguments(lib):
+    sink = ctypes.c_void_p(0x100000)
+    assert lib.router_probe_mfma(0, sink, 1 << 20, None) == -1
+    assert lib.router_probe_mfma(100, None, 1 << 20, None) == -1
+    assert lib.router_probe_mfma(100, sink, 1000, None) == -1  # sink smaller than one float per thread
+    assert lib.router_probe_mfma(1 << 25, sink, 1 << 20, None) == -1

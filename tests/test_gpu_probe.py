@@ -24,3 +24,14 @@ def test_probe_reads_every_word(nbytes, sink_words):
     got = np.bitwise_xor.reduce(sink[:grid].cpu().numpy())
     want = np.bitwise_xor.reduce(buf.cpu().numpy())
     assert got == want
+
+
+def test_mfma_probe_runs_the_same_work_everywhere():
+    dev = torch.device("cuda:0")
+    rt.load_library()
+    sink = torch.full((rt.MFMA_PROBE_SINK,), float("nan"), dtype=torch.float32, device=dev)
+    rt.probe_mfma(64, sink)
+    torch.cuda.synchronize()
+    v = sink.cpu().numpy().reshape(1024, 256)
+    assert np.all(np.isfinite(v))
+    assert np.all(v == v[0][None, :])  # every workgroup computed the same sums
