@@ -15,7 +15,13 @@ launched on; the eager rate and the two-call path (router_quantize, then
 router_gate_topk) are reported alongside. The roofline's `traffic` comes from
 the FETCH_SIZE / WRITE_SIZE counter summary committed under profiles/ and is
 null when the kernel sources have changed since it was taken. The CPU
-baseline is the oracle, timed on a bounded sample.
+baseline is the oracle, timed on a bounded sample, with the host's core
+count, CPU model and BLAS build.
+
+The decode line also carries a `prefill` block: the same metric at T=8192
+(D=7168, E=256, k=8), timed the same way, with the MFMA roofline of its gate
+kernel (FLOP over the event-timed launch duration) against the fp16 peak and
+against the library's MFMA probe. `--no-prefill` leaves it out.
 
 `--copy-calibration MiB` instead times a plain device-to-device copy of that
 size (the reference kernel for scaling the byte counters).
@@ -125,10 +131,12 @@ def cpu_baseline(cfg, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    # The oracle's only multi-threaded work is the BLAS matrix product, so the threads it actually uses are
+    # BLAS's (the rest of it is single-threaded numpy).
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
     except Exception:
         cores = 1
     return {"value": calls * rows / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
@@ -286,6 +294,162 @@ def lmhead_bench(torch, K, W, T=1, D=7168, N=129280):
         "cpu_baseline": None}), flush=True)
 
 
+def path_dtype(c):
+    """The arithmetic each gate path computes in (the operands stay NVFP4 throughout)."""
+    if c.T <= 4:
+        return "nvfp4 operands, exact f16 products on the VALU (v_dot2), f32 accumulate"
+    if c.T <= 256:
+        return "nvfp4 operands, exact f16 products on 16x16x32 f16 MFMA, f32 accumulate"
+    return "nvfp4 operands, exact f16 products on 32x32x16 f16 MFMA, f32 accumulate"
+
+
+class RouterBench:
+    """One router shape made resident on the GPU, with the timing helpers its measurements share."""
+
+    def __init__(self, torch, rt, wl, cfg, K, W):
+        self.torch, self.rt, self.c, self.K, self.W = torch, rt, wl.CONFIGS[cfg], K, W
+        c, dev = self.c, torch.device("cuda:0")
+        log(f"workload cfg {c.cfg} {c.name}: T={c.T} D={c.D} E={c.E} k={c.k} layers={c.layers}")
+        self.ws = rt.Workspace.for_shapes([(c.T, c.D, c.E, c.k), (c.E, c.D, c.E, c.k)], dev)
+        self.wq, self.bias, self.xs = [], [], []
+        for l in range(c.layers):
+            w = torch.from_numpy(wl.make_w(c.cfg, l).view(np.int16)).to(dev)
+            self.wq.append(rt.quantize(w, self.ws))  # load time
+            del w
+            self.bias.append(torch.from_numpy(wl.make_bias(c.cfg, l)).to(dev))
+            self.xs.append(torch.from_numpy(wl.make_x(c.cfg, l).view(np.int16)).to(dev))
+        self.xq = rt.empty_nvfp4(c.T, c.D, dev)
+        self.out = (torch.empty((c.T, c.k), dtype=torch.int32, device=dev),
+                    torch.empty((c.T, c.k), dtype=torch.float32, device=dev), None)
+        torch.cuda.synchronize()
+        log("inputs resident")
+
+    def step_forward(self, i):
+        c, l = self.c, i % self.c.layers
+        self.rt.forward(self.xs[l], self.wq[l], self.bias[l], c.k, c.routed_scale, self.ws, xq=self.xq, out=self.out)
+
+    def step_two_calls(self, i):
+        c, l = self.c, i % self.c.layers
+        self.rt.quantize(self.xs[l], self.ws, out=self.xq)
+        self.rt.gate_topk(self.xq, self.wq[l], self.bias[l], c.k, c.routed_scale, self.ws, out=self.out)
+
+    def time_eager(self, step):
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(self.K):
+            step(self.W + i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def time_graph(self, step):
+        """(wall seconds, HIP-event seconds) of one replay of K captured steps."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(self.K):
+                    step(self.W + i)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()  # untimed warm replay
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream()  # replay() launches the graph on this stream
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(cur)
+        g.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        del g
+        return dt, e0.elapsed_time(e1) * 1e-3
+
+    def event_time(self, fn, n):
+        """Mean duration of n eager launches of fn, each bracketed by HIP events on the launch stream."""
+        torch = self.torch
+        cur = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record(cur)
+            fn(self.W + i)
+            ev[i][1].record(cur)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+    def run(self, eager_only):
+        """Warm-up, then the timed router calls. Returns the measured figures."""
+        c, K, rt = self.c, self.K, self.rt
+        for step in (self.step_forward, self.step_two_calls):
+            for i in range(self.W):
+                step(i)
+        self.torch.cuda.synchronize()
+        r = {"eager_fwd": self.time_eager(self.step_forward), "eager_two": self.time_eager(self.step_two_calls),
+             "graph_fwd": None, "graph_two": None, "ev_fwd": None}
+        log(f"eager: forward {r['eager_fwd'] / K * 1e6:.2f} us/call, quantize+gate "
+            f"{r['eager_two'] / K * 1e6:.2f} us/call")
+        if not eager_only:
+            r["graph_two"], _ = self.time_graph(self.step_two_calls)
+            r["graph_fwd"], r["ev_fwd"] = self.time_graph(self.step_forward)
+            log(f"graph: forward {r['graph_fwd'] / K * 1e6:.2f} us/call (events {r['ev_fwd'] / K * 1e6:.2f}), "
+                f"quantize+gate {r['graph_two'] / K * 1e6:.2f} us/call")
+        r["timed_s"] = r["eager_fwd"] if r["graph_fwd"] is None else r["graph_fwd"]
+        nk = min(K, 500)
+        r["tf"] = self.event_time(self.step_forward, nk)
+        r["tq"] = self.event_time(lambda i: rt.quantize(self.xs[i % c.layers], self.ws, out=self.xq), nk)
+        r["tg"] = self.event_time(lambda i: rt.gate_topk(self.xq, self.wq[i % c.layers], self.bias[i % c.layers],
+                                                         c.k, c.routed_scale, self.ws, out=self.out), nk)
+        log(f"launch times: forward {r['tf'] * 1e6:.2f} us, quantize {r['tq'] * 1e6:.2f} us, "
+            f"gate {r['tg'] * 1e6:.2f} us")
+        return r
+
+    def config_fields(self, r):
+        c, K = self.c, self.K
+        return {
+            "workload": f"{c.name} router T={c.T} D={c.D} E={c.E} k={c.k}, {c.layers} layer set(s) cycled",
+            "T": c.T, "D": c.D, "E": c.E, "k": c.k,
+            "entry": "router_forward",
+            "launch": "eager" if r["graph_fwd"] is None else "hipgraph",
+            "us_per_call": r["timed_s"] / K * 1e6,
+            "eager_us_per_call": r["eager_fwd"] / K * 1e6,
+            "two_call_us_per_call": (r["eager_two"] if r["graph_two"] is None else r["graph_two"]) / K * 1e6,
+            "forward_launch_us": r["tf"] * 1e6,
+            "quantize_launch_us": r["tq"] * 1e6,
+            "gate_launch_us": r["tg"] * 1e6,
+        }
+
+    def prefill_roofline(self, r):
+        """MFMA roofline of the prefill gate: its FLOP over its event-timed launch duration."""
+        c = self.c
+        achieved = gate_flops(c) / r["tg"] / 1e12
+        probe = mfma_probe_tflops(self.torch, self.rt)
+        return {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None, "kernel": "gate_mfma_kernel",
+                "kernel_launch_us": r["tg"] * 1e6, "algorithmic": f"{gate_flops(c)} FLOP per launch",
+                "mfma_probe_tflops": probe, "frac_of_mfma_probe": achieved / probe}
+
+
+def cpu_host_facts():
+    """Host facts for the CPU baseline: cores available to this process, CPU model, BLAS build and threads."""
+    facts = {"host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": None, "blas": None}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                facts["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+
+        facts["blas"] = [{k: i.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")}
+                         for i in threadpool_info()]
+    except Exception:
+        pass
+    return facts
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +459,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill block (T=8192) that the decode line carries by default")
     ap.add_argument("--cold", action="store_true",
                     help="also time router calls that each follow a 1 GiB read (weights no longer in the Infinity Cache)")
     ap.add_argument("--lmhead", action="store_true",
@@ -322,119 +488,24 @@ def main():
     rt.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    c = wl.CONFIGS[args.config]
     K, W = args.steps, args.warmup
-    log(f"workload cfg {c.cfg} {c.name}: T={c.T} D={c.D} E={c.E} k={c.k} layers={c.layers}")
-
-    ws = rt.Workspace.for_shapes([(c.T, c.D, c.E, c.k), (c.E, c.D, c.E, c.k)], dev)
-    wq, bias, xs = [], [], []
-    for l in range(c.layers):
-        w = torch.from_numpy(wl.make_w(c.cfg, l).view(np.int16)).to(dev)
-        wq.append(rt.quantize(w, ws))  # load time
-        del w
-        bias.append(torch.from_numpy(wl.make_bias(c.cfg, l)).to(dev))
-        xs.append(torch.from_numpy(wl.make_x(c.cfg, l).view(np.int16)).to(dev))
-    xq = rt.empty_nvfp4(c.T, c.D, dev)
-    out = (torch.empty((c.T, c.k), dtype=torch.int32, device=dev),
-           torch.empty((c.T, c.k), dtype=torch.float32, device=dev), None)
-    torch.cuda.synchronize()
-    log("inputs resident")
-
-    def step_forward(i):
-        l = i % c.layers
-        rt.forward(xs[l], wq[l], bias[l], c.k, c.routed_scale, ws, xq=xq, out=out)
-
-    def step_two_calls(i):
-        l = i % c.layers
-        rt.quantize(xs[l], ws, out=xq)
-        rt.gate_topk(xq, wq[l], bias[l], c.k, c.routed_scale, ws, out=out)
-
-    def time_eager(step):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(K):
-            step(W + i)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
-
-    def time_graph(step):
-        """(wall seconds, HIP-event seconds) of one replay of K captured steps."""
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                for i in range(K):
-                    step(W + i)
-        torch.cuda.current_stream().wait_stream(s)
-        g.replay()  # untimed warm replay
-        torch.cuda.synchronize()
-        cur = torch.cuda.current_stream()  # replay() launches the graph on this stream
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(cur)
-        g.replay()
-        e1.record(cur)
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-        del g
-        return dt, e0.elapsed_time(e1) * 1e-3
-
-
-    for step in (step_forward, step_two_calls):
-        for i in range(W):
-            step(i)
-    torch.cuda.synchronize()
-
-    eager_fwd = time_eager(step_forward)
-    eager_two = time_eager(step_two_calls)
-    log(f"eager: forward {eager_fwd / K * 1e6:.2f} us/call, quantize+gate {eager_two / K * 1e6:.2f} us/call")
-    graph_fwd = graph_two = None
-    ev_fwd = None
-    if not args.eager:
-        graph_two, _ = time_graph(step_two_calls)
-        graph_fwd, ev_fwd = time_graph(step_forward)
-        log(f"graph: forward {graph_fwd / K * 1e6:.2f} us/call (events {ev_fwd / K * 1e6:.2f}), "
-            f"quantize+gate {graph_two / K * 1e6:.2f} us/call")
-    timed_s = eager_fwd if graph_fwd is None else graph_fwd
-
-    # Per-launch durations from HIP events on the launch stream (eager launches).
-    nk = min(K, 500)
-    cur = torch.cuda.current_stream()
-
-    def event_time(fn):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
-        for i in range(nk):
-            ev[i][0].record(cur)
-            fn(W + i)
-            ev[i][1].record(cur)
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
-
-    tf = event_time(step_forward)
-    tq = event_time(lambda i: rt.quantize(xs[i % c.layers], ws, out=xq))
-    tg = event_time(lambda i: rt.gate_topk(xq, wq[i % c.layers], bias[i % c.layers], c.k, c.routed_scale, ws,
-                                           out=out))
-    log(f"launch times: forward {tf * 1e6:.2f} us, quantize {tq * 1e6:.2f} us, gate {tg * 1e6:.2f} us")
+    rb = RouterBench(torch, rt, wl, args.config, K, W)
+    c = rb.c
+    r = rb.run(args.eager)
 
     if c.T > 256:
-        achieved = gate_flops(c) / tg / 1e12
-        probe = mfma_probe_tflops(torch, rt)
-        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None, "kernel": "gate_mfma_kernel",
-                "algorithmic": f"{gate_flops(c)} FLOP per launch",
-                "mfma_probe_tflops": probe, "frac_of_mfma_probe": achieved / probe}
+        roof = rb.prefill_roofline(r)
     elif c.T > 4:
         # Batched decode: a few hundred MFLOP against a megabyte of weights; bytes bound it (in practice the
         # loads' and the handoff's latency).
-        achieved = gate_bytes(c) / tg / 1e9
+        achieved = gate_bytes(c) / r["tg"] / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gate_tile_kernel",
                 "algorithmic": f"{gate_bytes(c)} B per launch"}
     else:
         # One launch per step: the events around the timed replay give the average launch duration.
         nbytes = forward_bytes(c)
-        t_launch = tf if ev_fwd is None else ev_fwd / K
+        t_launch = r["tf"] if r["ev_fwd"] is None else r["ev_fwd"] / K
         achieved = nbytes / t_launch / 1e9
         traffic = committed_traffic() if (c.cfg == 2 and not args.eager) else None
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -442,7 +513,7 @@ def main():
                 "kernel": "gate_decode_kernel (quantizing; the whole call is one launch)",
                 "launch_us": t_launch * 1e6,
                 "algorithmic": f"{nbytes} B per launch",
-                "probe": probe_rates(torch, rt, c, nbytes, time_graph, K, t_launch, args.eager)}
+                "probe": probe_rates(torch, rt, c, nbytes, rb.time_graph, K, t_launch, args.eager)}
 
     cold = None
     if args.cold:
@@ -461,15 +532,15 @@ def main():
                     for i in range(100):
                         rt.probe_read(flush, sink)
                         if with_call:
-                            step_forward(W + i)
+                            rb.step_forward(W + i)
             torch.cuda.current_stream().wait_stream(s)
             g.replay()
             torch.cuda.synchronize()
-            c = torch.cuda.current_stream()
+            cs = torch.cuda.current_stream()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(c)
+            e0.record(cs)
             g.replay()
-            e1.record(c)
+            e1.record(cs)
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) * 1e-3
 
@@ -477,12 +548,12 @@ def main():
         del flush
         log(f"cold (after a 1 GiB read): forward {cold * 1e6:.2f} us per call")
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle")
-        cpu = cpu_baseline(c.cfg, args.cpu_seconds)
-
+    timed_s = r["timed_s"]
     ms = timed_s / K * 1e3
+    config = rb.config_fields(r)
+    if cold is not None:
+        config["cold_forward_launch_us"] = cold * 1e6
+    config["parallelism"] = "single GPU"
     line = {
         "metric": METRIC,
         "value": c.T * K / timed_s,
@@ -494,25 +565,29 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 operands, f16 MFMA, f32 accumulate",
+        "dtype": path_dtype(c),
         "data": "synthetic",
-        "config": {
-            "workload": f"{c.name} router T={c.T} D={c.D} E={c.E} k={c.k}, {c.layers} layer set(s) cycled",
-            "T": c.T, "D": c.D, "E": c.E, "k": c.k,
-            "entry": "router_forward",
-            "launch": "eager" if graph_fwd is None else "hipgraph",
-            "us_per_call": ms * 1e3,
-            "eager_us_per_call": eager_fwd / K * 1e6,
-            "two_call_us_per_call": (eager_two if graph_two is None else graph_two) / K * 1e6,
-            "forward_launch_us": tf * 1e6,
-            "quantize_launch_us": tq * 1e6,
-            "gate_launch_us": tg * 1e6,
-            **({"cold_forward_launch_us": cold * 1e6} if cold is not None else {}),
-            "parallelism": "single GPU",
-        },
+        "config": config,
         "roofline": roof,
-        "cpu_baseline": cpu,
     }
+
+    if c.T <= 4 and not args.no_prefill:
+        # The same metric at the prefill shape (T=8192, D=7168, E=256, k=8): tokens/s of router_forward and
+        # the MFMA roofline of its gate kernel, timed the same way with the same step counts.
+        del rb
+        torch.cuda.empty_cache()
+        pb = RouterBench(torch, rt, wl, 4, K, min(W, 5))
+        pr = pb.run(args.eager)
+        line["prefill"] = {"value": pb.c.T * K / pr["timed_s"], "unit": "tokens/s", "dtype": path_dtype(pb.c),
+                           "config": pb.config_fields(pr), "roofline": pb.prefill_roofline(pr)}
+        del pb
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(c.cfg, args.cpu_seconds)
+        cpu.update(cpu_host_facts())
+    line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

@@ -58,11 +58,17 @@ extern "C" {
 
 #define ROUTER_MAX_EXPERTS 512
 #define ROUTER_MAX_TOPK 32
+#define ROUTER_MAX_GATE_D (1 << 22) /* largest hidden size of a gate call */
 
 /*
  * Bytes of workspace that router_quantize and router_gate_topk need for a
  * call with these sizes (rows = T tokens, D hidden, E experts, k chosen).
- * One workspace sized by this function serves both calls.
+ * One workspace sized by this function serves both calls. The caller
+ * allocates it once, ahead of time, and reuses it for every call, so that no
+ * call allocates or synchronizes and a decode loop can be captured in a
+ * graph (commit df05289d, dsv4/layers/grouped_linear.py: the fixes that
+ * pre-allocate the output buffer and the expert-offset range buffer once at
+ * initialization instead of per call).
  *
  * The first 4096 bytes hold arrival counters, which must be zero before the
  * first call (allocate zero-filled memory or call router_workspace_init) and
@@ -74,7 +80,11 @@ size_t router_workspace_bytes(int64_t T, int64_t D, int64_t E, int64_t k);
 
 /*
  * Zero-fills `bytes` of `workspace` on `stream` with a kernel (no memset
- * node, so it may be captured). Needed once per workspace allocation.
+ * node, so it may be captured). Needed once per workspace allocation, at the
+ * same initialization time as the allocation itself (the pre-allocated
+ * buffers of commit df05289d, dsv4/layers/grouped_linear.py).
+ * ROUTER_EINVAL if `workspace` is NULL or not 4-byte aligned, or `bytes` is
+ * not a multiple of 4 (bytes == 0 does nothing).
  */
 int router_workspace_init(void* workspace, size_t bytes, void* stream);
 
@@ -115,8 +125,11 @@ int router_quantize(const void* x, int64_t rows, int64_t D, const float* gsa_ove
  *                            [E, D/16] and a device fp32 scalar.
  *   bias                     [E] fp32 selection bias.
  *   routed_scale             host fp32 factor applied after renormalization.
- *   T, D, E, k               T >= 0; D % 32 == 0; 1 <= E <= 512;
- *                            1 <= k <= min(E, 32).
+ *   T, D, E, k               T >= 0; 1 <= k <= E; D >= 16, D % 16 == 0
+ *                            (ROUTER_EINVAL otherwise). The gate kernels
+ *                            read K in 32-element chunks, so D % 32 != 0,
+ *                            D > ROUTER_MAX_GATE_D, E > 512 and k > 32 give
+ *                            ROUTER_EUNSUPPORTED.
  *   topk_idx                 [T, k] int32 out: experts by descending
  *                            s + bias, an exact tie going to the lower index.
  *   topk_w                   [T, k] fp32 out: routed_scale * s / sum(s) over
@@ -141,7 +154,8 @@ int router_gate_topk(const uint8_t* x_codes, const uint8_t* x_scales, const floa
  * the quantize kernels and then the gate kernels on the stream.
  *
  * Arguments as in the two calls above: x [T, D] bf16 (16-byte aligned);
- * x_codes (16-byte aligned), x_scales and gsa_out are outputs; D % 32 == 0.
+ * x_codes (16-byte aligned), x_scales and gsa_out are outputs; the size
+ * limits of router_gate_topk apply (ROUTER_EUNSUPPORTED beyond them).
  * The workspace must satisfy router_workspace_bytes(T, D, E, k).
  */
 int router_forward(const void* x, int64_t T, int64_t D, const float* gsa_override, uint8_t* x_codes,
@@ -149,7 +163,12 @@ int router_forward(const void* x, int64_t T, int64_t D, const float* gsa_overrid
                    const float* gsw, const float* bias, float routed_scale, int64_t E, int64_t k, int32_t* topk_idx,
                    float* topk_w, float* logits_out, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Static text for a status code. */
+/*
+ * Static text for a status code. The library reports every rejection as a
+ * return value and never synchronizes to report one (the zero-host-sync rule
+ * of commit df05289d, dsv4/layers/grouped_linear.py); this turns the value
+ * into a message. Unknown codes give "unknown status".
+ */
 const char* router_status_string(int status);
 
 /*

@@ -378,11 +378,18 @@ constexpr int epi_rows() { return KS == 2 && BM >= 64 && J16 <= 24 ? 64 : 32; }
 template <int BM, int J16, int KS>
 constexpr int epi_sets() { return KS == 2 ? epi_rows<BM, J16, KS>() / 32 : 1; }
 
+// LDS row stride of the epilogue's logits, in floats: the router reads 16 J16
+// entries per row (16 bytes at a time), and the accumulators of a whole
+// expert block (128 NTW columns, zeros past E) are written there, so the row
+// holds the wider of the two.
+template <int NTW, int J16>
+constexpr int epi_ld() { return (16 * J16 > 128 * NTW ? 16 * J16 : 128 * NTW) + 4; }
+
 template <int BM, int NTW, int J16, int KS>
 union MmaLds {
   _Float16 abuf[KS][2][BM * kMmaARow];  // K loop: each K group's converted A tiles, double-buffered
   struct {
-    float lg[epi_rows<BM, J16, KS>() * (16 * J16 + 4)];           // epilogue: one pass's logits
+    float lg[epi_rows<BM, J16, KS>() * epi_ld<NTW, J16>()];       // epilogue: one pass's logits
     Row16Scratch<J16, epi_sets<BM, J16, KS>()> rsc[4 * KS];        // one router scratch per wavefront
   } epi;
 };
@@ -395,7 +402,7 @@ union MmaLds {
 template <int BM, int NTW, int J16, int KS>
 __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_eu(KS, KS))) void gate_mfma_kernel(
     MmaArgs m) {
-  constexpr int ldE = 16 * J16 + 4;  // the router reads 16 J16 entries per row, 16 bytes at a time
+  constexpr int ldE = epi_ld<NTW, J16>();
   static_assert(sizeof(MmaLds<BM, NTW, J16, KS>) + 512 * sizeof(float) + 16 <= 160 * 1024,
                 "LDS of one workgroup must fit a compute unit");
   const TileArgs& a = m.t;

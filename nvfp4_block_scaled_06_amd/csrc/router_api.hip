@@ -73,9 +73,13 @@ int check_gate_args(const uint8_t* x_codes, const uint8_t* x_scales, const float
                     const uint8_t* w_scales, const float* gsw, const float* bias, int64_t T, int64_t D, int64_t E,
                     int64_t k, const int32_t* topk_idx, const float* topk_w, const float* logits_out,
                     const void* workspace, size_t workspace_bytes) {
-  if (!shape_ok(T, D) || D % 32 != 0) return ROUTER_EINVAL;
+  if (!shape_ok(T, D)) return ROUTER_EINVAL;
   if (E < 1 || k < 1 || k > E) return ROUTER_EINVAL;
-  if (E > ROUTER_MAX_EXPERTS || k > ROUTER_MAX_TOPK) return ROUTER_EUNSUPPORTED;
+  // The gate kernels read K in 32-element chunks (two whole blocks), and the
+  // prefill kernel addresses one expert block's weight rows with 32-bit
+  // buffer offsets (512 rows of D / 2 bytes stay below 2^31 up to D = 2^22).
+  if (E > ROUTER_MAX_EXPERTS || k > ROUTER_MAX_TOPK || D % 32 != 0 || D > ROUTER_MAX_GATE_D)
+    return ROUTER_EUNSUPPORTED;
   if (!gsa || !w_codes || !w_scales || !gsw || !bias) return ROUTER_EINVAL;
   if (T > 0 && (!x_codes || !x_scales || !topk_idx || !topk_w)) return ROUTER_EINVAL;
   if (!aligned(x_codes, 16) || !aligned(w_codes, 16) || !aligned(x_scales, 2) || !aligned(w_scales, 2) ||
@@ -139,7 +143,7 @@ const char* router_status_string(int status) {
   switch (status) {
     case ROUTER_OK: return "ok";
     case ROUTER_EINVAL: return "invalid argument (shape, null or misaligned pointer, or workspace too small)";
-    case ROUTER_EUNSUPPORTED: return "unsupported size (E > 512 or k > 32)";
+    case ROUTER_EUNSUPPORTED: return "unsupported size (E > 512, k > 32, or a gate call with D % 32 != 0 or D > 2^22)";
     case ROUTER_EHIP: return "HIP launch error";
     default: return "unknown status";
   }

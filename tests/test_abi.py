@@ -43,6 +43,7 @@ def test_status_strings(lib):
     for s in (-1, -2, -3):
         assert lib.router_status_string(s) not in (b"ok", b"unknown status")
     assert lib.router_status_string(7) == b"unknown status"
+    assert b"D % 32" in lib.router_status_string(-2)
 
 
 def test_workspace_bytes(lib):
@@ -81,7 +82,9 @@ def test_gate_rejects_bad_arguments(lib):
         a = dict(args, **kw)
         return g(*a.values())
 
-    assert call(D=7184) == -1  # D % 32
+    assert call(D=7176) == -1  # D % 16
+    assert call(D=7184) == -2  # D % 32: documented as unsupported by the gate kernels
+    assert call(D=(1 << 22) + 32, T=300) == -2  # beyond ROUTER_MAX_GATE_D
     assert call(k=0) == -1 and call(k=257) == -1
     assert call(E=600, k=8) == -2
     assert call(k=33, E=256) == -2

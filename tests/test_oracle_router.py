@@ -24,6 +24,41 @@ def test_one_hot_logits():
     assert float(wq[2]) == 1.0
     L, A = logits_ref(*xq, *wq)
     assert L[0].tolist() == case["expect_logits"]
+    assert A[0].tolist() == case["expect_A"]
+
+
+def test_cancelling_logit_pins_the_tolerance_scale():
+    """A (the scale every logit tolerance is taken against) on a hand case where L cancels and A does not."""
+    case = GOLD["cancelling_logit"]
+    x = bf16_exact(case["x"])[None, :]
+    w = np.stack([bf16_exact(r) for r in case["w"]])
+    xq, wq = quantize_ref(x), quantize_ref(w)
+    assert float(xq[2]) == 1.0 and float(wq[2]) == 1.0
+    assert xq[1][0].tolist() == [0x7E, 0x58]  # S = 448 and 16
+    assert wq[1][0].tolist() == [0x7E, 0x69]  # S = 448 and 72
+    L, A = logits_ref(*xq, *wq)
+    assert L[0].tolist() == case["expect_logits"]
+    assert A[0].tolist() == case["expect_A"]
+    # A row's L1 norms multiplied together would inflate A (and loosen every logit check) here.
+    xv = np.abs(np.array([2688.0, 2688.0, 96.0]))
+    assert float(xv.sum() * (2688 + 2688 + 432)) != A[0, 0]
+
+
+def test_tolerance_scale_matches_exact_absolute_products():
+    """A against exact rational sums of |xhat| |what| on the tiny config (independent of the matrix product)."""
+    x, w = wl.make_x(1), wl.make_w(1)
+    xq, wq = quantize_ref(x), quantize_ref(w)
+    _, A = logits_ref(*xq, *wq)
+    ux, uw = unpack_codes(xq[0]).astype(int), unpack_codes(wq[0]).astype(int)
+    gx, gw = Fraction(float(xq[2])), Fraction(float(wq[2]))
+    for t in range(x.shape[0]):
+        for e in (0, 5, 15):
+            acc = Fraction(0)
+            for d in range(x.shape[1]):
+                vx = Fraction(float(E2M1_GRID[ux[t, d] & 7])) * Fraction(float(E4M3_GRID[xq[1][t, d // 16]]))
+                vw = Fraction(float(E2M1_GRID[uw[e, d] & 7])) * Fraction(float(E4M3_GRID[wq[1][e, d // 16]]))
+                acc += vx * vw
+            assert abs(Fraction(float(A[t, e])) - acc * gx * gw) <= acc * gx * gw * Fraction(1, 2 ** 45)
 
 
 def _logits_integer_form(xq, wq):
