@@ -55,10 +55,12 @@ extern "C" {
 #define ROUTER_EINVAL (-1)       /* bad shape, null or misaligned pointer, workspace too small */
 #define ROUTER_EUNSUPPORTED (-2) /* a documented size limit is exceeded */
 #define ROUTER_EHIP (-3)         /* a kernel launch reported an error */
+#define ROUTER_ESCRATCH (-4)     /* router_forward_noalloc: the call needs more than the static scratch */
 
 #define ROUTER_MAX_EXPERTS 512
 #define ROUTER_MAX_TOPK 32
 #define ROUTER_MAX_GATE_D (1 << 22) /* largest hidden size of a gate call */
+#define ROUTER_STATIC_SCRATCH_BYTES (16 << 20) /* router_forward_noalloc's scratch, per GPU */
 
 /*
  * Bytes of workspace that router_quantize and router_gate_topk need for a
@@ -162,6 +164,29 @@ int router_forward(const void* x, int64_t T, int64_t D, const float* gsa_overrid
                    uint8_t* x_scales, float* gsa_out, const uint8_t* w_codes, const uint8_t* w_scales,
                    const float* gsw, const float* bias, float routed_scale, int64_t E, int64_t k, int32_t* topk_idx,
                    float* topk_w, float* logits_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * router_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). It takes the same arguments as
+ * router_forward minus the workspace and gives the same results from the same
+ * kernels. Its scratch is a static device array of
+ * ROUTER_STATIC_SCRATCH_BYTES (16 MiB) that each GPU the library runs on
+ * holds until the process ends; the call itself allocates nothing and calls
+ * no allocating routine. The first call on a device looks up that array's
+ * address and enqueues one clear of its counters on `stream`.
+ *
+ * Calls whose router_workspace_bytes(T, D, E, k) exceeds 16 MiB (prefill
+ * batches whose experts are split over workgroups with T * E * 4 above it,
+ * e.g. T = 16384 at E = 256) return ROUTER_ESCRATCH before any launch;
+ * invalid or unsupported sizes give router_forward's status. Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give wrong results; enqueue them in order.
+ */
+int router_forward_noalloc(const void* x, int64_t T, int64_t D, const float* gsa_override, uint8_t* x_codes,
+                           uint8_t* x_scales, float* gsa_out, const uint8_t* w_codes, const uint8_t* w_scales,
+                           const float* gsw, const float* bias, float routed_scale, int64_t E, int64_t k,
+                           int32_t* topk_idx, float* topk_w, float* logits_out, void* stream);
 
 /*
  * Static text for a status code. The library reports every rejection as a

@@ -5,6 +5,8 @@
 #include "../../include/nvfp4_router.h"
 #include "router_internal.hpp"
 
+#include <mutex>
+
 namespace {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -145,8 +147,67 @@ const char* router_status_string(int status) {
     case ROUTER_EINVAL: return "invalid argument (shape, null or misaligned pointer, or workspace too small)";
     case ROUTER_EUNSUPPORTED: return "unsupported size (E > 512, k > 32, or a gate call with D % 32 != 0 or D > 2^22)";
     case ROUTER_EHIP: return "HIP launch error";
+    case ROUTER_ESCRATCH:
+      return "the call needs more scratch than the library's static buffer holds (ROUTER_STATIC_SCRATCH_BYTES = "
+             "16 MiB); use router_forward with a workspace";
     default: return "unknown status";
   }
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// router_forward_noalloc: router_forward with the library's own scratch, for
+// callers that cannot allocate. The scratch is one static device array per
+// GPU (it lives as long as the process). Host code never passes the array's
+// name to a kernel: `scratch` names a host-side stand-in there. Its device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[ROUTER_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's `scratch`, set up on its first
+// use: the symbol's address, then one clear of the part every call expects
+// zero between calls (the counters; static storage starts zeroed, and every
+// call leaves them zero, so this clear only makes that state explicit). The
+// clear is a kernel on the caller's stream, ordered before the call it
+// precedes.
+int static_scratch(void** out, hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ROUTER_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ROUTER_EHIP;
+    if (nvr::launch_fill_zero(p, nvr::kCounterBytes, stream) != hipSuccess) return ROUTER_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ROUTER_OK;
+}
+
+}  // namespace
+
+extern "C" int router_forward_noalloc(const void* x, int64_t T, int64_t D, const float* gsa_override,
+                                      uint8_t* x_codes, uint8_t* x_scales, float* gsa_out, const uint8_t* w_codes,
+                                      const uint8_t* w_scales, const float* gsw, const float* bias,
+                                      float routed_scale, int64_t E, int64_t k, int32_t* topk_idx, float* topk_w,
+                                      float* logits_out, void* stream) {
+  const size_t need = router_workspace_bytes(T, D, E, k);
+  if (need == 0) {  // invalid or unsupported sizes: router_forward says which, before any launch
+    return router_forward(x, T, D, gsa_override, x_codes, x_scales, gsa_out, w_codes, w_scales, gsw, bias,
+                          routed_scale, E, k, topk_idx, topk_w, logits_out, nullptr, 0, stream);
+  }
+  if (need > ROUTER_STATIC_SCRATCH_BYTES) return ROUTER_ESCRATCH;
+  void* ws = nullptr;
+  const int st = static_scratch(&ws, static_cast<hipStream_t>(stream));
+  if (st != ROUTER_OK) return st;
+  return router_forward(x, T, D, gsa_override, x_codes, x_scales, gsa_out, w_codes, w_scales, gsw, bias,
+                        routed_scale, E, k, topk_idx, topk_w, logits_out, ws, ROUTER_STATIC_SCRATCH_BYTES, stream);
+}

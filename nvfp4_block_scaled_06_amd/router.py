@@ -16,8 +16,10 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4_router.so")
 
 ROUTER_OK = 0
 EXPORTS = ("router_workspace_bytes", "router_workspace_init", "router_quantize", "router_gate_topk",
-           "router_forward", "router_status_string", "router_probe_read", "router_probe_mfma",
-           "lmhead_workspace_bytes", "lmhead_argmax")
+           "router_forward", "router_forward_noalloc", "router_status_string", "router_probe_read",
+           "router_probe_mfma", "lmhead_workspace_bytes", "lmhead_argmax")
+ROUTER_ESCRATCH = -4
+STATIC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -47,6 +49,9 @@ def load_library(path=LIB_PATH):
     L.router_forward.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, i64, i64, vp, vp,
                                  vp, vp, sz, vp]
     L.router_forward.restype = ctypes.c_int
+    L.router_forward_noalloc.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, i64, i64, vp,
+                                         vp, vp, vp]
+    L.router_forward_noalloc.restype = ctypes.c_int
     L.router_status_string.argtypes = [ctypes.c_int]
     L.router_status_string.restype = ctypes.c_char_p
     L.router_probe_read.argtypes = [vp, sz, vp, sz, vp]
@@ -193,6 +198,33 @@ def forward(x, wq, bias, k, routed_scale, workspace, gsa_override=None, want_log
                                          _ptr(xq.gscale), _ptr(wq.codes), _ptr(wq.scales), _ptr(wq.gscale),
                                          _ptr(bias), float(routed_scale), E, k, _ptr(idx), _ptr(w), _ptr(logits),
                                          _ptr(workspace.buf), workspace.nbytes, _stream()))
+    return xq, out
+
+
+def forward_noalloc(x, wq, bias, k, routed_scale, gsa_override=None, want_logits=False, xq=None, out=None):
+    """router_forward_noalloc: router_forward with the library's static scratch instead of a workspace.
+
+    Same arguments and results as ``forward`` without ``workspace``; raises RouterError with status -4 when the
+    call needs more than the 16 MiB static scratch."""
+    _device_tensor(x, "x", (torch.bfloat16, torch.int16, torch.uint16), ndim=2)
+    T, D = x.shape
+    E = wq.rows
+    _device_tensor(bias, "bias", (torch.float32,), ndim=1)
+    if wq.D != D or bias.numel() != E:
+        raise RouterError("gate weights / bias do not match x")
+    if gsa_override is not None:
+        _device_tensor(gsa_override, "gsa_override", (torch.float32,))
+    if xq is None:
+        xq = empty_nvfp4(T, D, x.device)
+    if out is None:
+        dev = x.device
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None)
+    idx, w, logits = out
+    _check(load_library().router_forward_noalloc(_ptr(x), T, D, _ptr(gsa_override), _ptr(xq.codes),
+                                                 _ptr(xq.scales), _ptr(xq.gscale), _ptr(wq.codes), _ptr(wq.scales),
+                                                 _ptr(wq.gscale), _ptr(bias), float(routed_scale), E, k, _ptr(idx),
+                                                 _ptr(w), _ptr(logits), _stream()))
     return xq, out
 
 

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     assert lib.router_status_string(0) == b"ok"
-    for s in (-1, -2, -3):
+    for s in (-1, -2, -3, -4):
         assert lib.router_status_string(s) not in (b"ok", b"unknown status")
     assert lib.router_status_string(7) == b"unknown status"
     assert b"D % 32" in lib.router_status_string(-2)
@@ -130,3 +130,17 @@ def test_mfma_probe_rejects_bad_arguments(lib):
     assert lib.router_probe_mfma(100, None, 1 << 20, None) == -1
     assert lib.router_probe_mfma(100, sink, 1000, None) == -1  # sink smaller than one float per thread
     assert lib.router_probe_mfma(1 << 25, sink, 1 << 20, None) == -1
+
+
+def test_noalloc_rejects_sizes_beyond_its_static_scratch(lib):
+    """router_forward_noalloc refuses, before touching the GPU, a call whose scratch exceeds the 16 MiB array,
+    and passes invalid sizes on to router_forward's own checks."""
+    T, D, E, k = 16384, 7168, 256, 8  # prefill with split experts: [T, E] fp32 logits = 16 MiB + counters
+    assert lib.router_workspace_bytes(T, D, E, k) > rt.STATIC_SCRATCH_BYTES
+    args = [FAKE, T, D, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2.5, E, k, FAKE, FAKE, None, None]
+    assert lib.router_forward_noalloc(*args) == rt.ROUTER_ESCRATCH
+    assert b"16 MiB" in lib.router_status_string(rt.ROUTER_ESCRATCH)
+    bad = list(args); bad[2] = 7176  # D % 16
+    assert lib.router_forward_noalloc(*bad) == -1
+    bad = list(args); bad[1] = 1; bad[12] = 600  # E > 512
+    assert lib.router_forward_noalloc(*bad) == -2
