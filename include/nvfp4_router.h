@@ -61,6 +61,7 @@ extern "C" {
 #define ROUTER_MAX_TOPK 32
 #define ROUTER_MAX_GATE_D (1 << 22) /* largest hidden size of a gate call */
 #define ROUTER_STATIC_SCRATCH_BYTES (16 << 20) /* router_forward_noalloc's scratch, per GPU */
+#define ROUTER_WORKSPACE_STATE_BYTES (4096 + 131072) /* workspace prefix that stays zero between calls */
 
 /*
  * Bytes of workspace that router_quantize and router_gate_topk need for a
@@ -72,11 +73,13 @@ extern "C" {
  * pre-allocate the output buffer and the expert-offset range buffer once at
  * initialization instead of per call).
  *
- * The first 4096 bytes hold arrival counters, which must be zero before the
- * first call (allocate zero-filled memory or call router_workspace_init) and
- * which every call leaves zero again; the rest is per-call scratch. Calls
- * that share one workspace must be ordered (one stream); concurrent calls
- * need workspaces of their own. Returns 0 for invalid sizes.
+ * The first ROUTER_WORKSPACE_STATE_BYTES bytes (arrival counters and the
+ * decode gate's flagged partials) must be zero before the first call
+ * (allocate zero-filled memory or call router_workspace_init), and every call
+ * leaves them zero again; the rest is per-call scratch. Every size this
+ * function returns covers that state. Calls that share one workspace must be
+ * ordered (one stream); concurrent calls need workspaces of their own.
+ * Returns 0 for invalid sizes.
  */
 size_t router_workspace_bytes(int64_t T, int64_t D, int64_t E, int64_t k);
 
@@ -216,9 +219,10 @@ const char* router_status_string(int status);
  *                            logit.
  *   logits_out               NULL, or [T, N] fp32 out: every logit.
  *   workspace                256-byte aligned, lmhead_workspace_bytes(T, D,
- *                            N) bytes; its first 4096 bytes are the arrival
- *                            counters shared with the router calls (zero
- *                            between calls, see router_workspace_bytes).
+ *                            N) bytes; its first
+ *                            ROUTER_WORKSPACE_STATE_BYTES bytes are the state
+ *                            shared with the router calls (zero between
+ *                            calls, see router_workspace_bytes).
  * Returns ROUTER_EINVAL for bad shapes, pointers or workspace.
  */
 size_t lmhead_workspace_bytes(int64_t T, int64_t D, int64_t N);

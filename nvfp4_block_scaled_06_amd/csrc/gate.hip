@@ -703,7 +703,7 @@ static hipError_t launch_mma(const TileArgs& a, hipStream_t stream) {
 
 size_t gate_scratch_bytes(int64_t T, int64_t D, int64_t E) {
   switch (gate_kind(T, D)) {
-    case GateKind::kDecode: return decode_scratch_bytes(T, D, E);
+    case GateKind::kDecode: return 0;  // the decode region below kScratchOffset
     case GateKind::kTile: return (size_t)T * (size_t)E * sizeof(float);
     default: return plan_mma(T, E).ncb > 1 ? (size_t)T * (size_t)E * sizeof(float) : 0;
   }
@@ -711,12 +711,13 @@ size_t gate_scratch_bytes(int64_t T, int64_t D, int64_t E) {
 
 hipError_t launch_gate(const uint8_t* xc, const uint8_t* xs, const float* gsa, const uint8_t* wc, const uint8_t* ws,
                        const float* gsw, const float* bias, float rs, int64_t T, int64_t D, int64_t E, int64_t k,
-                       int32_t* idx, float* w, float* lo, uint32_t* counters, void* scratch, hipStream_t stream) {
+                       int32_t* idx, float* w, float* lo, void* workspace, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const GateKind kind = gate_kind(T, D);
-  float* lbuf = static_cast<float*>(scratch);
   if (kind == GateKind::kDecode)
-    return launch_decode_gate(xc, xs, gsa, wc, ws, gsw, bias, rs, T, D, E, k, idx, w, lo, lbuf, counters, stream);
+    return launch_decode_gate(xc, xs, gsa, wc, ws, gsw, bias, rs, T, D, E, k, idx, w, lo, workspace, stream);
+  uint32_t* counters = static_cast<uint32_t*>(workspace);
+  float* lbuf = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kScratchOffset) : nullptr;
   TileArgs a{xc, xs, gsa, wc, ws, gsw, bias, rs, (int)T, (int)D, (int)E, (int)k, idx, w, lo, lbuf, counters,
              (int)((D + 127) / 128)};
   return kind == GateKind::kTile ? launch_tile(a, stream) : launch_mma(a, stream);

@@ -368,7 +368,8 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
 
 constexpr int kRouteFastSurvivors = 32;
 
-// LDS scratch of one wavefront's router.
+// LDS scratch of one wavefront's router; entry 64 JMAX of cand / cs is a
+// spare slot that absorbs the writes of keys that do not survive.
 template <int JMAX>
 struct WaveRouteScratch {
   uint64_t cand[64 * JMAX + 8];
@@ -376,6 +377,47 @@ struct WaveRouteScratch {
   float sel_s[64];
   int sel_i[32];
 };
+
+// Row broadcasts of the wave-wide reductions (lane 15 of rows 0 and 2 into
+// rows 1 and 3; lane 31 into rows 2 and 3); rows not written keep `id`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_bcast(uint32_t v, uint32_t id) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWS, 0xF, false);
+}
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+// Smallest value over the wavefront, for values already equal within each
+// aligned group of GL lanes (GL = 2, 4, 8 or 16): the other groups of each
+// row (pairs into quads, quads into eights, eights into rows), then the rows;
+// read from lane 63.
+template <int GL>
+__device__ __forceinline__ uint32_t wave_min_of_groups(uint32_t v) {
+  if constexpr (GL <= 2) v = min(v, dpp_u<kDppXor2>(v));
+  if constexpr (GL <= 4) v = min(v, dpp_u<kDppHalfMirror>(v));
+  if constexpr (GL <= 8) v = min(v, dpp_u<kDppMirror>(v));
+  v = min(v, dpp_bcast<kDppRowBcast15, 0xA>(v, 0xFFFFFFFFu));
+  v = min(v, dpp_bcast<kDppRowBcast31, 0xC>(v, 0xFFFFFFFFu));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Sum over the wavefront in a fixed order (deterministic), left in lane 63.
+__device__ __forceinline__ float wave_sum_bcast(float v) {
+  v += __int_as_float(dpp_i<kDppXor1>(__float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppXor2>(__float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppMirror>(__float_as_int(v)));
+  v += __uint_as_float(dpp_bcast<kDppRowBcast15, 0xA>(__float_as_uint(v), 0u));
+  v += __uint_as_float(dpp_bcast<kDppRowBcast31, 0xC>(__float_as_uint(v), 0u));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// The value this lane's partner in the other half of the wavefront holds
+// (lane l and l +- 32): one v_permlane32_swap.
+__device__ __forceinline__ uint32_t other_half(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
 
 // Six-step routing of one token by one wavefront (commit e0f60b9f,
 // dsv4/kernels/router/__init__.py: the single-pass activation/top-k
@@ -385,15 +427,18 @@ struct WaveRouteScratch {
 // w *= routed_scale.
 //
 // Lane l holds experts l, l+64, ... (JMAX of them). Selection without k
-// serial rounds:
+// serial rounds, and without divergent branches on the usual path:
 //  1. every lane forms s and the order-preserving score key of its experts;
 //  2. the lanes form G >= k aligned groups; the smallest group maximum is a
 //     lower bound on the k-th largest key (the G group maxima are G >= k
 //     distinct experts at or above it), so experts below it cannot be chosen;
 //  3. the survivors (at least k, typically a few more) are compacted into LDS
-//     by ballot and each one's exact rank among them is counted: larger key
-//     first, lower expert first on equal keys, i.e. the larger (key, ~expert)
-//     pair. Survivors outrank every other expert, so that is the global rank;
+//     by ballot (the others write a spare slot) and each one's exact rank
+//     among them is counted: larger key first, lower expert first on equal
+//     keys, i.e. the larger (key, ~expert) pair. Survivors outrank every
+//     other expert, so that is the global rank. With at most 32 survivors,
+//     lanes l and l + 32 both take survivor l, each against half of the list,
+//     and add their counts across the halves;
 //  4. ranks below k are the chosen list, already sorted; the weights use a
 //     fixed-order (DPP tree) sum of the chosen s.
 // One wavefront, no workgroup barrier: LDS traffic of a single wave is
@@ -408,63 +453,62 @@ __device__ __forceinline__ void wave_route_regs(const float (&L)[JMAX], const fl
 #pragma unroll
   for (int j = 0; j < JMAX; ++j) {
     s[j] = sigmoid_fast(L[j]);
-    key[j] = (lane + 64 * j < E) ? score_key(s[j] + bv[j]) : 0u;
+    const uint32_t kk = score_key(s[j] + bv[j]);
+    key[j] = lane + 64 * j < E ? kk : 0u;
   }
   uint32_t lm = key[0];
 #pragma unroll
   for (int j = 1; j < JMAX; ++j) lm = max(lm, key[j]);
-  // Groups of GL lanes, GL the largest power of two with 64 / GL >= k.
-  uint32_t gmax;
-  if (k <= 4) gmax = group_max_u32<16>(lm);
-  else if (k <= 8) gmax = group_max_u32<8>(lm);
-  else if (k <= 16) gmax = group_max_u32<4>(lm);
-  else if (k <= 32) gmax = group_max_u32<2>(lm);
-  else gmax = lm;
-  if (k <= 4) {  // 4 groups of 16 lanes: fold pairs of rows as well
+  // Groups of GL lanes, GL the largest power of two with 64 / GL >= k (up to
+  // 16: one DPP row); fewer than four groups take row maxima and fold them.
+  uint32_t tau;
+  if (k > 4) {
+    if (k <= 8) tau = wave_min_of_groups<8>(group_max_u32<8>(lm));
+    else if (k <= 16) tau = wave_min_of_groups<4>(group_max_u32<4>(lm));
+    else tau = wave_min_of_groups<2>(group_max_u32<2>(lm));
+  } else {
+    const uint32_t gmax = group_max_u32<16>(lm);
     const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)gmax, 0);
     const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)gmax, 16);
     const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)gmax, 32);
     const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)gmax, 48);
     const uint32_t g01 = max(r0, r1), g23 = max(r2, r3);
-    gmax = k <= 2 ? (lane < 32 ? g01 : g23) : gmax;
-    gmax = k <= 1 ? max(g01, g23) : gmax;
+    tau = k <= 1 ? max(g01, g23) : (k <= 2 ? min(g01, g23) : min(min(r0, r1), min(r2, r3)));
   }
-  const uint32_t tau = wave_min_u32(gmax);
 
-  // Compact the survivors.
+  // Compact the survivors: each writes its slot, the others the spare one.
+  constexpr int kSpare = 64 * JMAX;
   int C = 0;
 #pragma unroll
   for (int j = 0; j < JMAX; ++j) {
     const bool cand = key[j] != 0u && key[j] >= tau;
     const uint64_t bal = __ballot(cand);
-    if (cand) {
-      const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-      sc.cand[pos] = ((uint64_t)key[j] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * j));
-      sc.cs[pos] = s[j];
-    }
+    const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    const int slot = cand ? pos : kSpare;
+    sc.cand[slot] = ((uint64_t)key[j] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * j));
+    sc.cs[slot] = s[j];
     C += (int)__popcll(bal);
   }
   const float rsc = routed_scale;
   if (C <= kRouteFastSurvivors) {
-    // Usual case: every survivor is ranked against all others with one batch
-    // of LDS reads (entries past C are zero and rank below everything), the
-    // weight sum is a DPP tree over the chosen lanes, and each chosen lane
-    // stores its own output at its rank.
+    // Usual case. Entries C .. 31 are zero and rank below everything.
     if (lane >= C && lane < kRouteFastSurvivors) sc.cand[lane] = 0ull;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    uint64_t all[kRouteFastSurvivors];
+    const int u = lane & 31, half = lane >> 5;
+    const uint64_t mine = sc.cand[u];
+    const float ms = sc.cs[u];
+    uint64_t part[16];
 #pragma unroll
-    for (int u = 0; u < kRouteFastSurvivors; ++u) all[u] = sc.cand[u];
-    const uint64_t mine = sc.cand[lane & (kRouteFastSurvivors - 1)];
-    const float ms = sc.cs[lane & (kRouteFastSurvivors - 1)];
+    for (int i = 0; i < 16; ++i) part[i] = sc.cand[16 * half + i];
     int rank = 0;
 #pragma unroll
-    for (int u = 0; u < kRouteFastSurvivors; ++u) rank += all[u] > mine ? 1 : 0;
-    const bool chosen = lane < C && rank < k;
-    const float ssum = wave_sum(chosen ? ms : 0.0f);
+    for (int i = 0; i < 16; ++i) rank += part[i] > mine ? 1 : 0;
+    rank += (int)other_half((uint32_t)rank);
+    const bool chosen = lane < C && lane < 32 && rank < k;
+    const float ssum = wave_sum_bcast(chosen ? ms : 0.0f);
     if (chosen) {
       out_idx[rank] = (int)(0xFFFFFFFFu - (uint32_t)mine);
       out_w[rank] = ms * (rsc * __builtin_amdgcn_rcpf(ssum));
@@ -484,9 +528,9 @@ __device__ __forceinline__ void wave_route_regs(const float (&L)[JMAX], const fl
     for (int c0 = 0; c0 < C; c0 += 8) {
       uint64_t v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = sc.cand[c0 + u];
+      for (int q = 0; q < 8; ++q) v[q] = sc.cand[c0 + q];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) rank += v[u] > mine ? 1 : 0;
+      for (int q = 0; q < 8; ++q) rank += v[q] > mine ? 1 : 0;
     }
     if (c < C && rank < k) {
       sc.sel_i[rank] = (int)(0xFFFFFFFFu - (uint32_t)mine);
@@ -498,7 +542,7 @@ __device__ __forceinline__ void wave_route_regs(const float (&L)[JMAX], const fl
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const float sv = lane < k ? sc.sel_s[min(lane, 63)] : 0.0f;
   const int si = sc.sel_i[min(lane, 31)];
-  const float ssum = wave_sum(sv);
+  const float ssum = wave_sum_bcast(sv);
   if (lane < k) {
     out_idx[lane] = si;
     out_w[lane] = sv * (rsc * __builtin_amdgcn_rcpf(ssum));

@@ -7,6 +7,8 @@
 
 #include <mutex>
 
+static_assert(nvr::kScratchOffset == ROUTER_WORKSPACE_STATE_BYTES, "the documented zero-state prefix");
+
 namespace {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -27,7 +29,7 @@ size_t gate_need(int64_t T, int64_t D, int64_t E) {
   if (T == 0) return 0;
   const size_t scratch = nvr::gate_scratch_bytes(T, D, E);
   if (nvr::gate_kind(T, D) == nvr::GateKind::kMma && scratch == 0) return 0;  // no counters, no scratch
-  return nvr::kScratchOffset + scratch;
+  return nvr::kScratchOffset + scratch;  // the decode gate needs the regions below kScratchOffset only
 }
 
 size_t quantize_need(int64_t rows, int64_t D, bool override_given) {
@@ -103,10 +105,8 @@ int router_gate_topk(const uint8_t* x_codes, const uint8_t* x_scales, const floa
                                  logits_out, workspace, workspace_bytes);
   if (st != ROUTER_OK) return st;
   const bool ws = gate_need(T, D, E) > 0;
-  uint32_t* counters = ws ? static_cast<uint32_t*>(workspace) : nullptr;
-  void* scratch = ws ? static_cast<char*>(workspace) + nvr::kScratchOffset : nullptr;
   return status_from(nvr::launch_gate(x_codes, x_scales, gsa, w_codes, w_scales, gsw, bias, routed_scale, T, D, E,
-                                      k, topk_idx, topk_w, logits_out, counters, scratch,
+                                      k, topk_idx, topk_w, logits_out, ws ? workspace : nullptr,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -127,8 +127,8 @@ int router_forward(const void* x, int64_t T, int64_t D, const float* gsa_overrid
   char* base = static_cast<char*>(workspace);
   if (T > 0 && nvr::forward_single_launch(T, D)) {
     return status_from(nvr::launch_forward_fused(x, gsa_override, x_codes, x_scales, gsa_out, w_codes, w_scales, gsw,
-                                                 bias, routed_scale, T, D, E, k, topk_idx, topk_w, logits_out,
-                                                 reinterpret_cast<uint32_t*>(base), base + nvr::kScratchOffset, s));
+                                                 bias, routed_scale, T, D, E, k, topk_idx, topk_w, logits_out, base,
+                                                 s));
   }
   // Larger T: the quantize kernels then the gate kernels, back to back on the stream.
   hipError_t err = nvr::launch_quantize(x, T, D, gsa_override, x_codes, x_scales, gsa_out,
@@ -136,9 +136,7 @@ int router_forward(const void* x, int64_t T, int64_t D, const float* gsa_overrid
   if (err != hipSuccess) return ROUTER_EHIP;
   const bool ws = gate_need(T, D, E) > 0;
   return status_from(nvr::launch_gate(x_codes, x_scales, gsa_out, w_codes, w_scales, gsw, bias, routed_scale, T, D,
-                                      E, k, topk_idx, topk_w, logits_out,
-                                      ws ? reinterpret_cast<uint32_t*>(base) : nullptr,
-                                      ws ? base + nvr::kScratchOffset : nullptr, s));
+                                      E, k, topk_idx, topk_w, logits_out, ws ? workspace : nullptr, s));
 }
 
 const char* router_status_string(int status) {
@@ -174,10 +172,10 @@ void* g_scratch_ptr[kMaxDevices] = {};
 
 // The device address of the current device's `scratch`, set up on its first
 // use: the symbol's address, then one clear of the part every call expects
-// zero between calls (the counters; static storage starts zeroed, and every
-// call leaves them zero, so this clear only makes that state explicit). The
-// clear is a kernel on the caller's stream, ordered before the call it
-// precedes.
+// zero between calls (the counters and the decode region; static storage
+// starts zeroed, and every call leaves them zero, so this clear only makes
+// that state explicit). The clear is a kernel on the caller's stream, ordered
+// before the call it precedes.
 int static_scratch(void** out, hipStream_t stream) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ROUTER_EHIP;
@@ -185,7 +183,7 @@ int static_scratch(void** out, hipStream_t stream) {
   if (g_scratch_ptr[dev] == nullptr) {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ROUTER_EHIP;
-    if (nvr::launch_fill_zero(p, nvr::kCounterBytes, stream) != hipSuccess) return ROUTER_EHIP;
+    if (nvr::launch_fill_zero(p, nvr::kScratchOffset, stream) != hipSuccess) return ROUTER_EHIP;
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];

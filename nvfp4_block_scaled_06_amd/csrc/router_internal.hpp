@@ -10,15 +10,22 @@ namespace nvr {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Workspace layout:
-//   [0, kCounterBytes)     arrival counters of the decode and tile gates:
-//                          zero between calls (every call that counts
-//                          returns its counter to zero);
+//   [0, kCounterBytes)     arrival counters of the tile and split-expert
+//                          gates and the lm_head: zero between calls (every
+//                          call that counts returns its counter to zero);
+//   [kDecodeRegionOffset, kScratchOffset)
+//                          the decode gate's flagged slice partials: zero
+//                          between calls (the call that writes a word also
+//                          clears it), and written by no other kernel;
 //   [kScratchOffset, ...)  per-call scratch (partial maxima of the quantizer,
-//                          the slice partials of the decode gate, the [T, E]
-//                          logits of the tile gate).
+//                          the [T, E] logits of the tile gate and of the
+//                          split-expert prefill gate, the lm_head's
+//                          per-workgroup candidates).
 constexpr size_t kCounterBytes = 4096;
 constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(uint32_t));
-constexpr size_t kScratchOffset = kCounterBytes;
+constexpr size_t kDecodeRegionOffset = kCounterBytes;
+constexpr size_t kDecodeRegionBytes = 128 * 1024;
+constexpr size_t kScratchOffset = kDecodeRegionOffset + kDecodeRegionBytes;
 
 constexpr int kSingleWgMaxBlocks = 2048;  // single-workgroup quantizer up to this many blocks
 constexpr int kAmaxPartials = 1024;       // workgroups of the amax pass
@@ -49,23 +56,22 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_gate(const uint8_t* x_codes, const uint8_t* x_scales, const float* gsa, const uint8_t* w_codes,
                        const uint8_t* w_scales, const float* gsw, const float* bias, float routed_scale, int64_t T,
                        int64_t D, int64_t E, int64_t k, int32_t* topk_idx, float* topk_w, float* logits_out,
-                       uint32_t* counters, void* scratch, hipStream_t stream);
+                       void* workspace, hipStream_t stream);
 
-// Decode-size gate (gate_decode.hip): whether T x D takes it, its scratch,
-// and its launch (reading quantized x).
+// Decode-size gate (gate_decode.hip): whether T x D takes it, and its launch
+// (reading quantized x). It uses the workspace's decode region only.
 bool decode_fits(int64_t T, int64_t D);
-size_t decode_scratch_bytes(int64_t T, int64_t D, int64_t E);
 hipError_t launch_decode_gate(const uint8_t* x_codes, const uint8_t* x_scales, const float* gsa,
                               const uint8_t* w_codes, const uint8_t* w_scales, const float* gsw, const float* bias,
                               float routed_scale, int64_t T, int64_t D, int64_t E, int64_t k, int32_t* topk_idx,
-                              float* topk_w, float* logits_out, float* lbuf, uint32_t* counters, hipStream_t stream);
+                              float* topk_w, float* logits_out, void* workspace, hipStream_t stream);
 
 // Quantize + gate in one launch (decode-size T only; see forward_single_launch).
 bool forward_single_launch(int64_t T, int64_t D);
 hipError_t launch_forward_fused(const void* x, const float* gsa_override, uint8_t* x_codes, uint8_t* x_scales,
                                 float* gsa_out, const uint8_t* w_codes, const uint8_t* w_scales, const float* gsw,
                                 const float* bias, float routed_scale, int64_t T, int64_t D, int64_t E, int64_t k,
-                                int32_t* topk_idx, float* topk_w, float* logits_out, uint32_t* counters,
-                                void* scratch, hipStream_t stream);
+                                int32_t* topk_idx, float* topk_w, float* logits_out, void* workspace,
+                                hipStream_t stream);
 
 }  // namespace nvr

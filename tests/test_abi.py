@@ -46,13 +46,16 @@ def test_status_strings(lib):
     assert b"D % 32" in lib.router_status_string(-2)
 
 
+STATE = 4096 + 128 * 1024  # counters + the decode region: zero between calls
+
+
 def test_workspace_bytes(lib):
     n = lib.router_workspace_bytes(1, 7168, 256, 8)
-    assert n >= 4096 + 4096 and n % 4 == 0
+    assert n >= STATE and n % 4 == 0
     assert lib.router_workspace_bytes(64, 7168, 256, 8) >= lib.router_workspace_bytes(1, 7168, 256, 8)
-    assert lib.router_workspace_bytes(8192, 7168, 256, 8) == 4096 + 8192 * 256 * 4  # split experts: [T, E] logits
-    assert lib.router_workspace_bytes(32768, 7168, 384, 8) == 4096 + 4096  # all experts per workgroup: quantizer only
-    assert lib.router_workspace_bytes(1, 7168, 256, 8) == 4096 + 7 * 256 * 4  # decode: 7 K slices of partials
+    assert lib.router_workspace_bytes(8192, 7168, 256, 8) == STATE + 8192 * 256 * 4  # split experts: [T, E] logits
+    assert lib.router_workspace_bytes(32768, 7168, 384, 8) == STATE + 4096  # all experts per workgroup: quantizer only
+    assert lib.router_workspace_bytes(1, 7168, 256, 8) == STATE + 4096  # decode: its region, and the quantizer's
     for bad in [(1, 7168, 256, 0), (1, 7168, 256, 257), (1, 7169, 256, 8), (-1, 7168, 256, 8), (1, 7168, 0, 1),
                 (1, 7168, 513, 8)]:
         assert lib.router_workspace_bytes(*bad) == 0, bad
@@ -106,8 +109,8 @@ def test_probe_rejects_bad_arguments(lib):
 
 def test_lmhead_workspace_and_validation(lib):
     # counters + one 8-byte candidate per token and 64-row workgroup
-    assert lib.lmhead_workspace_bytes(1, 7168, 129280) == 4096 + 8 * 2020
-    assert lib.lmhead_workspace_bytes(4, 7168, 65) == 4096 + 8 * 4 * 2
+    assert lib.lmhead_workspace_bytes(1, 7168, 129280) == STATE + 8 * 2020
+    assert lib.lmhead_workspace_bytes(4, 7168, 65) == STATE + 8 * 4 * 2
     for bad in [(5, 7168, 10), (1, 7160, 10), (1, 16416, 10), (1, 7168, 0), (-1, 7168, 10), (4, 16384, 10)]:
         assert lib.lmhead_workspace_bytes(*bad) == 0, bad
     p = ctypes.c_void_p(0x100000)
