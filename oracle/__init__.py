@@ -16,7 +16,8 @@ repository; they are cited by commit and by the paragraph a fact sits in):
 * commit e0f60b9f, ``dsv4/kernels/router/__init__.py`` -- the working path:
   gate GEMM then a single-pass six-step activation/top-k epilogue.
 * commit df05289d, ``dsv4/layers/grouped_linear.py`` -- device-only global
-  scale, no host syncs, caller-owned pre-allocated buffers.
+  scale, no host syncs, caller-owned pre-allocated buffers, the grouped
+  layer's flattened quantization and device-side group offsets.
 
 Facts the pages leave open are fixed by the NVFP4 format (16-element blocks
 along the contraction axis, E4M3 block scales, E2M1 elements, one fp32
@@ -34,6 +35,9 @@ Parity status per function:
 * ``check``: pinned by mutation tests (planted mistakes must be caught).
 * ``lmhead_ref``: pinned (one-hot hand case with a tie, brute force over
   rows, mutation tests of its checker); its logits are router_ref's.
+* ``grouped_ref``: pinned (hand cases with per-group weight scales and a
+  shared activation scale set by another group, offsets closed form, exact
+  rational brute force on tiny groups, empty groups).
 
 Two conventions are not fixed by the pages and are parity unpinned by them:
 the nibble order of packed codes (even element in the low nibble) and the
@@ -41,4 +45,4 @@ code of -0 and of negatives that round to zero (sign kept: 0x8). The tests
 pin the oracle to these stated conventions.
 """
 
-from . import formats, quant_ref, router_ref, check, lmhead_ref  # noqa: F401
+from . import formats, quant_ref, router_ref, check, lmhead_ref, grouped_ref  # noqa: F401
