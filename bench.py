@@ -294,6 +294,92 @@ def lmhead_bench(torch, K, W, T=1, D=7168, N=129280):
         "cpu_baseline": None}), flush=True)
 
 
+def grouped_bench(torch, gcfg, K, W):
+    """The grouped NVFP4 layer (grouped_offsets + router_quantize over the flattened groups + grouped_gemm)
+    on a GroupedConfig: K calls graph-replayed after W warm-ups, weights resident and quantized beforehand.
+    Prints one JSON line; the roofline is the GEMM kernel's: HBM bytes at decode size (the weight stream),
+    fp16 MFMA FLOP at prefill size."""
+    from nvfp4_block_scaled_06_amd import router as rt
+    from nvfp4_block_scaled_06_amd import workloads as wl
+
+    rt.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = wl.GROUPED_CONFIGS[gcfg]
+    R = c.G * c.P
+    log(f"grouped layer {c.name}: G={c.G} P={c.P} D={c.D} N={c.N}")
+    ws = rt.Workspace(max(rt.workspace_bytes(R, c.D, 16, 1), rt.workspace_bytes(c.N, c.D, 16, 1)), dev)
+    w = torch.from_numpy(np.stack([wl.make_grouped_w(gcfg, g) for g in range(c.G)]).view(np.int16)).to(dev)
+    wg = rt.quantize_grouped_weights(w, ws)  # load time
+    del w
+    x = torch.from_numpy(wl.make_grouped_x(gcfg).view(np.int16)).to(dev)
+    rng_buf = torch.arange(c.G + 1, dtype=torch.int32, device=dev)  # allocated once, reused
+    off = torch.empty(c.G + 1, dtype=torch.int32, device=dev)
+    xq = rt.empty_nvfp4(R, c.D, dev)
+    out = torch.empty((R, c.N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        rt.grouped_offsets(rng_buf, c.P, out=off)
+        rt.quantize(x, ws, out=xq)
+        rt.grouped_gemm(xq, wg, off, c.P, out=out)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for _ in range(K):
+                step()
+    torch.cuda.current_stream().wait_stream(st)
+    g.replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(cur)
+    g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t = e0.elapsed_time(e1) * 1e-3 / K
+    # The GEMM kernel alone, event-timed per launch.
+    n = min(K, 200)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(cur)
+        rt.grouped_gemm(xq, wg, off, c.P, out=out)
+        b.record(cur)
+    torch.cuda.synchronize()
+    tk = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    flops = 2 * R * c.N * c.D
+    nbytes = c.G * c.N * c.D * 9 // 16 + 4 * c.G + R * c.D * 9 // 16 + 4 + 4 * (c.G + 1) + 4 * R * c.N
+    if c.P <= 4:
+        achieved = nbytes / tk / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "grouped_mfma_kernel",
+                "kernel_launch_us": tk * 1e6, "algorithmic": f"{nbytes} B per launch"}
+    else:
+        achieved = flops / tk / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None, "kernel": "grouped_mfma_kernel",
+                "kernel_launch_us": tk * 1e6, "algorithmic": f"{flops} FLOP per launch"}
+    log(f"{c.name}: {t * 1e6:.2f} us per call (offsets + quantize + GEMM); GEMM {tk * 1e6:.2f} us, "
+        f"{roof['achieved']:.0f} {roof['unit']}")
+    print(json.dumps({
+        "metric": f"grouped NVFP4 layer rows/s, G={c.G} P={c.P} D={c.D} N={c.N}", "value": R / t, "unit": "rows/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": wall / K * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4 operands, exact f16 products on 32x32x16 f16 MFMA, f32 accumulate", "data": "synthetic",
+        "config": {"workload": f"{c.name} G={c.G} P={c.P} D={c.D} N={c.N}",
+                   "entry": "grouped_offsets + router_quantize + grouped_gemm", "launch": "hipgraph",
+                   "us_per_call": t * 1e6, "gemm_launch_us": tk * 1e6},
+        "roofline": roof, "cpu_baseline": None}), flush=True)
+
+
 def path_dtype(c):
     """The arithmetic each gate path computes in (the operands stay NVFP4 throughout)."""
     if c.T <= 4:
@@ -465,6 +551,8 @@ def main():
                     help="also time router calls that each follow a 1 GiB read (weights no longer in the Infinity Cache)")
     ap.add_argument("--lmhead", action="store_true",
                     help="time the greedy NVFP4 lm_head (129280 x 7168, T=1) instead of the router")
+    ap.add_argument("--grouped", type=int, default=0, metavar="CFG",
+                    help="time the grouped NVFP4 layer instead of the router (12 = decode size, 13 = prefill size)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="time a plain device copy of this many MiB instead of the router")
     args = ap.parse_args()
@@ -480,6 +568,9 @@ def main():
         return
     if args.lmhead:
         lmhead_bench(torch, min(args.steps, 200), min(args.warmup, 20))
+        return
+    if args.grouped:
+        grouped_bench(torch, args.grouped, min(args.steps, 200), min(args.warmup, 20))
         return
 
     from nvfp4_block_scaled_06_amd import router as rt

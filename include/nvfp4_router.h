@@ -231,6 +231,50 @@ int lmhead_argmax(const uint8_t* x_codes, const uint8_t* x_scales, const float* 
                   float* out_logit, float* logits_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Group offsets of the grouped linear layer, on the device: offsets[g] =
+ * range[g] * padded_rows for g = 0 .. G (G + 1 values), group g owning rows
+ * offsets[g] .. offsets[g + 1] - 1 of the flattened activations. `range` is a
+ * caller-owned device buffer of G + 1 int32 holding 0, 1, ..., G, filled once
+ * at initialization and reused; computing the offsets from it on the device
+ * is the fix of commit df05289d (dsv4/layers/grouped_linear.py, Section A
+ * detector items 2 and 5) that removes the host loop, its per-group host
+ * sync and the per-call allocation. One kernel launch on `stream`.
+ *   1 <= G <= 2^24, padded_rows >= 0, G * padded_rows < 2^31; 4-byte aligned
+ *   pointers; ROUTER_EINVAL otherwise.
+ */
+int grouped_offsets(const int32_t* range, int64_t G, int64_t padded_rows, int32_t* offsets, void* stream);
+
+/*
+ * Grouped NVFP4 GEMM (the grouped linear layer of commit df05289d,
+ * dsv4/layers/grouped_linear.py): for every row r of group g,
+ *   out[r, n] = gsa * gsw[g] * sum_d xhat[r, d] * what_g[n, d]
+ * with fp32 accumulation over exact fp16 products (the gate's arithmetic).
+ *
+ *   x_codes, x_scales, gsa   router_quantize outputs for the flattened
+ *                            activations of all groups, [R, D] (one launch,
+ *                            one global scale: the pages' fused quantize
+ *                            over (G * T, D)).
+ *   w_codes, w_scales, gsw   the groups' weights, [G, N, D/2], [G, N, D/16]
+ *                            (each group row-major (N, K_packed), as in the
+ *                            checkpoint) and [G] fp32 device scales.
+ *   offsets                  [G + 1] int32 device (e.g. from
+ *                            grouped_offsets): 0 = offsets[0] <= ... <=
+ *                            offsets[G] <= R. Values outside are clamped
+ *                            (their rows are not defined).
+ *   max_rows                 host bound on any group's row count; rows of a
+ *                            group past max_rows are not computed. For the
+ *                            padded layout it is padded_rows.
+ *   out                      [R, N] fp32; rows of no group are not written.
+ * Code pointers 16-byte, scale pointers 2-byte, the rest 4-byte aligned.
+ * ROUTER_EINVAL for bad sizes or pointers; ROUTER_EUNSUPPORTED for D % 32 !=
+ * 0, D > ROUTER_MAX_GATE_D or a grid beyond 2^31 workgroups. One launch on
+ * `stream`, no workspace, no host sync: capturable.
+ */
+int grouped_gemm(const uint8_t* x_codes, const uint8_t* x_scales, const float* gsa, const uint8_t* w_codes,
+                 const uint8_t* w_scales, const float* gsw, const int32_t* offsets, int64_t G, int64_t R,
+                 int64_t max_rows, int64_t N, int64_t D, float* out, void* stream);
+
+/*
  * Measurement aid, not part of the router path: reads `bytes` of `buf`
  * (device, 16-byte aligned, bytes % 16 == 0) once with 16-byte loads in one
  * launch of min(bytes / 4096 rounded up, sink_words, 8192) workgroups of 256

@@ -25,7 +25,7 @@
 // lane here loads 32 consecutive elements (16 code bytes, 2 scale bytes) of
 // its row and feeds them to four successive MFMAs, 8 at a time: a
 // permutation of K that A and B share, so every product meets its partner.
-#include "gate_common.hpp"
+#include "mma_tile.hpp"
 
 #include <stdlib.h>
 
@@ -168,207 +168,12 @@ __global__ __launch_bounds__(kTileThreads) void gate_tile_kernel(TileArgs a) {
 // Workgroups are numbered so that the NCB expert blocks of a token block run
 // on one XCD (x fetched from HBM once, shared in its L2).
 // ---------------------------------------------------------------------------
-constexpr int kMmaThreads = 256;
-
-// K steps of loads in flight: four for the small tiles, two when the
-// accumulators and weight fragments of a wide tile already need most registers.
-template <int BM, int NTW>
-constexpr int mma_ring() {
-  return (BM / 32) * NTW >= 6 ? 2 : 4;
-}
-constexpr int kMmaARow = 136;  // LDS row stride of the A tile in halves (128 values + 8 pad)
-
 struct MmaArgs {
   TileArgs t;
   int ncb;     // expert blocks (workgroups per token block)
   int nwg;     // workgroups
   int nsteps;  // 128-element K steps, rounded up to a multiple of K groups times the ring depth
 };
-
-// Token rows per thread in the A tile (4 threads per row): one slot per 64
-// rows; with BM = 32 only threads 0..127 have a row.
-template <int BM>
-constexpr int mma_row_slots() {
-  return BM >= 64 ? BM / 64 : 1;
-}
-
-template <int BM, int NTW>
-struct MmaRegs {
-  u32x4_t a[mma_row_slots<BM>()];  // A: this thread's 32-element chunk of rows tid/4 (+ 64 i)
-  uint32_t as[mma_row_slots<BM>()];
-  u32x4_t b[NTW][2];   // B: this lane's two chunks per expert tile
-  uint32_t bs[NTW][2];
-};
-
-// Operand reads are raw buffer loads: each workgroup's descriptors cover
-// only its token rows and its expert rows, and a read past a descriptor's
-// end returns zeros. Rows past T or E and chunks past D (given an
-// out-of-range offset) therefore load zeros without a branch, so the wait
-// counters of the load ring stay exact. Offsets are per lane; a step adds 64
-// code bytes and 8 scale bytes.
-constexpr uint32_t kMmaOob = 0x80000000u;  // beyond every descriptor's range
-constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
-}
-
-template <int BM, int NTW>
-struct MmaPtrs {
-  __amdgpu_buffer_rsrc_t xc, xs, wc, ws;
-  uint32_t a[mma_row_slots<BM>()], as[mma_row_slots<BM>()];
-  uint32_t b[NTW], bs[NTW];
-  int ka, kb;  // K offset of this thread's A chunk / this lane's first B chunk within a step
-};
-
-template <int BM, int NTW>
-__device__ __forceinline__ MmaPtrs<BM, NTW> mma_ptrs(const TileArgs& a, int row0, int col0, int wave, int lane) {
-  MmaPtrs<BM, NTW> P;
-  const int tid = threadIdx.x & (kMmaThreads - 1), q = tid & 3, r = lane & 31, h = lane >> 5;
-  const int64_t rowc = a.D / 2, rows = a.D / 16;
-  const int64_t nr = min((int64_t)BM, (int64_t)a.T - row0), nc = min((int64_t)128 * NTW, (int64_t)a.E - col0);
-  P.xc = make_rsrc(a.xc + row0 * rowc, nr * rowc);
-  P.xs = make_rsrc(a.xs + row0 * rows, nr * rows);
-  P.wc = make_rsrc(a.wc + col0 * rowc, nc * rowc);
-  P.ws = make_rsrc(a.ws + col0 * rows, nc * rows);
-  P.ka = 32 * q;
-  P.kb = 32 * h;
-#pragma unroll
-  for (int i = 0; i < mma_row_slots<BM>(); ++i) {
-    const int rl = (tid >> 2) + 64 * i;  // row within the tile
-    P.a[i] = rl < BM ? (uint32_t)(rl * rowc + 16 * q) : kMmaOob;
-    P.as[i] = rl < BM ? (uint32_t)(rl * rows + 2 * q) : kMmaOob;
-  }
-#pragma unroll
-  for (int t = 0; t < NTW; ++t) {
-    const int el = (wave + 4 * t) * 32 + r;  // expert within the block
-    P.b[t] = (uint32_t)(el * rowc + 16 * h);
-    P.bs[t] = (uint32_t)(el * rows + 2 * h);
-  }
-  return P;
-}
-
-template <int BM, int NTW>
-__device__ __forceinline__ void mma_load(MmaRegs<BM, NTW>& R, const MmaPtrs<BM, NTW>& P, int D, int step) {
-  const int k0 = step * 128;
-  const bool aok = k0 + P.ka < D;
-#pragma unroll
-  for (int i = 0; i < mma_row_slots<BM>(); ++i) {
-    const uint32_t oc = aok ? P.a[i] + 64 * step : kMmaOob, os = aok ? P.as[i] + 8 * step : kMmaOob;
-    R.a[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(P.xc, oc, 0, 0));
-    R.as[i] = __builtin_amdgcn_raw_buffer_load_b16(P.xs, os, 0, 0);
-  }
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const bool bok = k0 + 64 * c + P.kb < D;
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      const uint32_t oc = bok ? P.b[t] + 64 * step + 32 * c : kMmaOob;
-      const uint32_t os = bok ? P.bs[t] + 8 * step + 4 * c : kMmaOob;
-      R.b[t][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(P.wc, oc, 0, 0));
-      R.bs[t][c] = __builtin_amdgcn_raw_buffer_load_b16(P.ws, os, 0, 0);
-    }
-  }
-}
-
-// This thread's A chunks, converted, into the LDS tile.
-template <int BM, int NTW>
-__device__ __forceinline__ void mma_store_a(const MmaRegs<BM, NTW>& R, _Float16* abuf) {
-  const int tid = threadIdx.x & (kMmaThreads - 1), q = tid & 3;
-#pragma unroll
-  for (int i = 0; i < mma_row_slots<BM>(); ++i) {
-    const int r = (tid >> 2) + 64 * i;
-    if (r >= BM) break;  // BM = 32: threads 128..255 hold no row
-    const _Float16 s0 = e4m3_f16(R.as[i] & 0xFFu), s1 = e4m3_f16(R.as[i] >> 8);
-    half8_t* dst = reinterpret_cast<half8_t*>(abuf + r * kMmaARow + 32 * q);
-    dst[0] = fp4x8_to_f16(R.a[i][0], s0);
-    dst[1] = fp4x8_to_f16(R.a[i][1], s0);
-    dst[2] = fp4x8_to_f16(R.a[i][2], s1);
-    dst[3] = fp4x8_to_f16(R.a[i][3], s1);
-  }
-}
-
-// Accumulator sets per output tile: two (MFMAs j < 4 and j >= 4 alternate
-// between them) when a wavefront has fewer than four tiles, so that enough
-// independent MFMAs are in flight; they are added at the end.
-template <int BM, int NTW>
-constexpr int mma_sets() {
-  return (BM / 32) * NTW < 4 ? 2 : 1;
-}
-
-// Two K groups (eight wavefronts) when a wavefront's accumulators leave room
-// for two wavefronts per SIMD.
-template <int BM, int NTW>
-constexpr int mma_ksplit() {
-  return (BM / 32) * NTW <= 2 ? 2 : 1;
-}
-
-// One step: the MFMAs of step s with A from the LDS tile and B converted
-// from this step's raw chunks (Rc) just ahead of the MFMAs of the first row
-// tile that use it, interleaved with the conversion of step s + 1's A
-// chunks (Rn) into the other LDS tile. A wavefront issues one instruction
-// every few clocks while an MFMA keeps the matrix core busy for 32, so each
-// MFMA is followed by a share of the conversion units (8 elements each) and,
-// in the two-group kernels, scheduling fences keep that order (measured: with
-// one K group the compiler's own order is 4 % faster at 128 tokens x 384
-// experts; with two groups the fences win). The A fragments of row tile
-// rt + 1 are read right after their last use in row tile rt.
-template <int BM, int NTW>
-__device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& Rc, const _Float16* abuf, const MmaRegs<BM, NTW>& Rn,
-                                         _Float16* abuf_n, int lane,
-                                         f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
-  constexpr int NS = mma_sets<BM, NTW>();
-  constexpr int SL = mma_row_slots<BM>();
-  constexpr int NM = (BM / 32) * 8 * NTW;  // MFMAs; the first 8 NTW use B units 0 .. 8 NTW - 1 in order
-  constexpr int NB = 8 * NTW;              // B units
-  constexpr int NA = 4 * SL;               // A units
-  const int r = lane & 31, h = lane >> 5;
-  const int tid = threadIdx.x & (kMmaThreads - 1), q4 = tid & 3;
-  _Float16 bsc[NTW][2][2], asc[SL][2];
-#pragma unroll
-  for (int t = 0; t < NTW; ++t)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bsc[t][c][0] = e4m3_f16(Rc.bs[t][c] & 0xFFu);
-      bsc[t][c][1] = e4m3_f16(Rc.bs[t][c] >> 8);
-    }
-#pragma unroll
-  for (int i = 0; i < SL; ++i) {
-    asc[i][0] = e4m3_f16(Rn.as[i] & 0xFFu);
-    asc[i][1] = e4m3_f16(Rn.as[i] >> 8);
-  }
-  half8_t B[NTW][8];
-  // B unit m feeds MFMA m of the first row tile: K slice j = m / NTW of
-  // expert tile t = m % NTW.
-  auto bunit = [&](auto uc) {
-    constexpr int m = decltype(uc)::value, j = m / NTW, t = m % NTW;
-    B[t][j] = fp4x8_to_f16(Rc.b[t][j / 4][j % 4], bsc[t][j / 4][(j % 4) >> 1]);
-  };
-  auto aunit = [&](auto uc) {
-    constexpr int i = decltype(uc)::value / 4, q = decltype(uc)::value % 4;
-    const int row = (tid >> 2) + 64 * i;
-    if (BM >= 64 || row < BM)  // BM = 32: threads 128..255 hold no row
-      reinterpret_cast<half8_t*>(abuf_n + row * kMmaARow + 32 * q4)[q] = fp4x8_to_f16(Rn.a[i][q], asc[i][q >> 1]);
-  };
-  const _Float16* arow = abuf + r * kMmaARow + 32 * h;
-  auto afrag = [&](int rt, int j) {
-    return *reinterpret_cast<const half8_t*>(arow + rt * 32 * kMmaARow + (j < 4 ? 8 * j : 64 + 8 * (j - 4)));
-  };
-  half8_t A[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) A[j] = afrag(0, j);
-  bunit(IntC<0>{});
-  static_for<0, NM>([&](auto mc) {
-    constexpr int m = decltype(mc)::value;
-    constexpr int rt = m / (8 * NTW), j = (m / NTW) % 8, t = m % NTW;
-    f32x16_t& c = acc[NS == 2 ? (j >> 2) : 0][rt][t];
-    c = mfma32(A[j], B[t][j], c);
-    if constexpr (t == NTW - 1 && rt + 1 < BM / 32) A[j] = afrag(rt + 1, j);
-    if constexpr (m + 1 < NB) bunit(IntC<m + 1>{});
-    static_for<(m * NA + NM - 1) / NM, ((m + 1) * NA + NM - 1) / NM>(aunit);
-    if constexpr (mma_ksplit<BM, NTW>() == 2) __builtin_amdgcn_sched_barrier(0);
-  });
-}
 
 // Epilogue rows per pass: 64 when two K groups share the work and the rows
 // fit the LDS, else 32. Each wavefront routes LR / (4 KS) rows per pass, as
@@ -424,44 +229,11 @@ __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_e
 
   constexpr int NS = mma_sets<BM, NTW>();
   f32x16_t acc[NS][BM / 32][NTW];
-#pragma unroll
-  for (int q = 0; q < NS; ++q)
-#pragma unroll
-    for (int rt = 0; rt < BM / 32; ++rt)
-#pragma unroll
-      for (int t = 0; t < NTW; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[q][rt][t][v] = 0.0f;
-
-  // Steps are padded to a multiple of KS times the ring depth: padding steps
-  // load nothing (k >= D) and add zeros.
-  const MmaPtrs<BM, NTW> P = mma_ptrs<BM, NTW>(a, row0, col0, wt, lane);
-  constexpr int RING = mma_ring<BM, NTW>();
-  MmaRegs<BM, NTW> R[RING];
-#pragma unroll
-  for (int p = 0; p < RING; ++p) mma_load<BM, NTW>(R[p], P, a.D, KS * p + grp);
-  mma_store_a<BM, NTW>(R[0], u.abuf[grp][0]);
-  __syncthreads();
-  for (int s0 = 0; s0 < nsteps; s0 += KS * RING) {
-    // The A tiles alternate with this group's step count, RING it + p: with
-    // an odd ring the parity of p alone does not alternate across passes.
-    const int par = (RING & 1) ? (s0 / (KS * RING)) & 1 : 0;
-#pragma unroll
-    for (int p = 0; p < RING; ++p) {
-      // Step s0 + KS p + grp: A from tile (p + par) & 1, B from R[p]; the
-      // next step's A (R[(p + 1) % RING]) into the other tile; then R[p]
-      // (fully used) reloads the step RING ahead.
-      mma_step<BM, NTW>(R[p], u.abuf[grp][(p + par) & 1], R[(p + 1) % RING], u.abuf[grp][(p + 1 + par) & 1], lane, acc);
-      mma_load<BM, NTW>(R[p], P, a.D, s0 + KS * (p + RING) + grp);
-      __syncthreads();
-    }
-  }
-  if (NS == 2) {
-#pragma unroll
-    for (int rt = 0; rt < BM / 32; ++rt)
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) acc[0][rt][t] += acc[NS - 1][rt][t];
-  }
+  const int64_t rowc = a.D / 2, rows = a.D / 16;
+  const MmaPtrs<BM, NTW> P = mma_ptrs<BM, NTW>(
+      a.xc + row0 * rowc, a.xs + row0 * rows, min((int64_t)BM, (int64_t)a.T - row0), a.wc + col0 * rowc,
+      a.ws + col0 * rows, min((int64_t)128 * NTW, (int64_t)a.E - col0), a.D, wt, lane);
+  mma_mainloop<BM, NTW, KS>(P, a.D, nsteps, &u.abuf[0][0][0], lane, acc);
 
   // Epilogue. 32x32 accumulator layout: value v of lane (r, h) is row
   // 8(v/4) + 4h + v%4, column r of its tile. With two K groups, group 1

@@ -1,0 +1,288 @@
+// MFMA tile machinery shared by the prefill gate and the grouped GEMM
+// (gfx950): a workgroup computes a BM x 128 NTW tile of products of two
+// NVFP4 operands (rows of [rows, D/2] codes and [rows, D/16] E4M3 scales),
+// both converted to exact fp16 q S values, on 32x32x16 f16 MFMAs.
+//
+//  * Tiles: four wavefronts per K group; wavefront w owns the 32-column
+//    tiles w, w + 4, ... and all BM rows. K advances 128 elements per step.
+//  * A (rows): each step's BM x 128 tile is converted once per workgroup
+//    (32 elements per thread and row) into an LDS tile of fp16 q S values,
+//    double-buffered, which every wavefront reads with ds_read_b128.
+//  * B (columns): each lane loads two 32-element chunks of its column row
+//    per step (16 code bytes + 2 scale bytes each) and converts them in
+//    registers; no other wavefront needs them.
+//  * K permutation: lane (r, h) of a 32x32x16 MFMA supplies 8 K values of
+//    row/column r from group h; in step-relative K, MFMA j (0..7) takes
+//    [32h + 8j, +8) for j < 4 and [64 + 32h + 8(j - 4), +8) for j >= 4, on A
+//    and on B alike, so every product meets its partner and each K value is
+//    used once. Every product is exact (at most 6 significant bits per
+//    operand), so only the fp32 accumulation rounds.
+//  * Loads are raw buffer loads whose descriptors cover only the tile's
+//    rows, so rows past the end and chunks past D read zeros without a
+//    branch; they run mma_ring() steps ahead in a register ring.
+#pragma once
+
+#include "gate_common.hpp"
+
+namespace nvr {
+
+constexpr int kMmaThreads = 256;
+
+// K steps of loads in flight: four for the small tiles, two when the
+// accumulators and weight fragments of a wide tile already need most registers.
+template <int BM, int NTW>
+constexpr int mma_ring() {
+  return (BM / 32) * NTW >= 6 ? 2 : 4;
+}
+constexpr int kMmaARow = 136;  // LDS row stride of the A tile in halves (128 values + 8 pad)
+
+
+// Token rows per thread in the A tile (4 threads per row): one slot per 64
+// rows; with BM = 32 only threads 0..127 have a row.
+template <int BM>
+constexpr int mma_row_slots() {
+  return BM >= 64 ? BM / 64 : 1;
+}
+
+template <int BM, int NTW>
+struct MmaRegs {
+  u32x4_t a[mma_row_slots<BM>()];  // A: this thread's 32-element chunk of rows tid/4 (+ 64 i)
+  uint32_t as[mma_row_slots<BM>()];
+  u32x4_t b[NTW][2];   // B: this lane's two chunks per expert tile
+  uint32_t bs[NTW][2];
+};
+
+// Operand reads are raw buffer loads: each workgroup's descriptors cover
+// only its token rows and its expert rows, and a read past a descriptor's
+// end returns zeros. Rows past T or E and chunks past D (given an
+// out-of-range offset) therefore load zeros without a branch, so the wait
+// counters of the load ring stay exact. Offsets are per lane; a step adds 64
+// code bytes and 8 scale bytes.
+constexpr uint32_t kMmaOob = 0x80000000u;  // beyond every descriptor's range
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+template <int BM, int NTW>
+struct MmaPtrs {
+  __amdgpu_buffer_rsrc_t xc, xs, wc, ws;
+  uint32_t a[mma_row_slots<BM>()], as[mma_row_slots<BM>()];
+  uint32_t b[NTW], bs[NTW];
+  int ka, kb;  // K offset of this thread's A chunk / this lane's first B chunk within a step
+};
+
+// Descriptors and per-lane offsets of one workgroup tile: its token (row)
+// tile starts at xc / xs and has nr valid rows, its weight (column) tile
+// starts at wc / ws and has nc valid rows; both are [rows, D / 2] codes and
+// [rows, D / 16] scales.
+template <int BM, int NTW>
+__device__ __forceinline__ MmaPtrs<BM, NTW> mma_ptrs(const uint8_t* xc, const uint8_t* xs, int64_t nr,
+                                                     const uint8_t* wc, const uint8_t* ws, int64_t nc, int64_t D,
+                                                     int wave, int lane) {
+  MmaPtrs<BM, NTW> P;
+  const int tid = threadIdx.x & (kMmaThreads - 1), q = tid & 3, r = lane & 31, h = lane >> 5;
+  const int64_t rowc = D / 2, rows = D / 16;
+  P.xc = make_rsrc(xc, nr * rowc);
+  P.xs = make_rsrc(xs, nr * rows);
+  P.wc = make_rsrc(wc, nc * rowc);
+  P.ws = make_rsrc(ws, nc * rows);
+  P.ka = 32 * q;
+  P.kb = 32 * h;
+#pragma unroll
+  for (int i = 0; i < mma_row_slots<BM>(); ++i) {
+    const int rl = (tid >> 2) + 64 * i;  // row within the tile
+    P.a[i] = rl < BM ? (uint32_t)(rl * rowc + 16 * q) : kMmaOob;
+    P.as[i] = rl < BM ? (uint32_t)(rl * rows + 2 * q) : kMmaOob;
+  }
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int el = (wave + 4 * t) * 32 + r;  // expert within the block
+    P.b[t] = (uint32_t)(el * rowc + 16 * h);
+    P.bs[t] = (uint32_t)(el * rows + 2 * h);
+  }
+  return P;
+}
+
+template <int BM, int NTW>
+__device__ __forceinline__ void mma_load(MmaRegs<BM, NTW>& R, const MmaPtrs<BM, NTW>& P, int D, int step) {
+  const int k0 = step * 128;
+  const bool aok = k0 + P.ka < D;
+#pragma unroll
+  for (int i = 0; i < mma_row_slots<BM>(); ++i) {
+    const uint32_t oc = aok ? P.a[i] + 64 * step : kMmaOob, os = aok ? P.as[i] + 8 * step : kMmaOob;
+    R.a[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(P.xc, oc, 0, 0));
+    R.as[i] = __builtin_amdgcn_raw_buffer_load_b16(P.xs, os, 0, 0);
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const bool bok = k0 + 64 * c + P.kb < D;
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const uint32_t oc = bok ? P.b[t] + 64 * step + 32 * c : kMmaOob;
+      const uint32_t os = bok ? P.bs[t] + 8 * step + 4 * c : kMmaOob;
+      R.b[t][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(P.wc, oc, 0, 0));
+      R.bs[t][c] = __builtin_amdgcn_raw_buffer_load_b16(P.ws, os, 0, 0);
+    }
+  }
+}
+
+// This thread's A chunks, converted, into the LDS tile.
+template <int BM, int NTW>
+__device__ __forceinline__ void mma_store_a(const MmaRegs<BM, NTW>& R, _Float16* abuf) {
+  const int tid = threadIdx.x & (kMmaThreads - 1), q = tid & 3;
+#pragma unroll
+  for (int i = 0; i < mma_row_slots<BM>(); ++i) {
+    const int r = (tid >> 2) + 64 * i;
+    if (r >= BM) break;  // BM = 32: threads 128..255 hold no row
+    const _Float16 s0 = e4m3_f16(R.as[i] & 0xFFu), s1 = e4m3_f16(R.as[i] >> 8);
+    half8_t* dst = reinterpret_cast<half8_t*>(abuf + r * kMmaARow + 32 * q);
+    dst[0] = fp4x8_to_f16(R.a[i][0], s0);
+    dst[1] = fp4x8_to_f16(R.a[i][1], s0);
+    dst[2] = fp4x8_to_f16(R.a[i][2], s1);
+    dst[3] = fp4x8_to_f16(R.a[i][3], s1);
+  }
+}
+
+// Accumulator sets per output tile: two (MFMAs j < 4 and j >= 4 alternate
+// between them) when a wavefront has fewer than four tiles, so that enough
+// independent MFMAs are in flight; they are added at the end.
+template <int BM, int NTW>
+constexpr int mma_sets() {
+  return (BM / 32) * NTW < 4 ? 2 : 1;
+}
+
+// Two K groups (eight wavefronts) when a wavefront's accumulators leave room
+// for two wavefronts per SIMD.
+template <int BM, int NTW>
+constexpr int mma_ksplit() {
+  return (BM / 32) * NTW <= 2 ? 2 : 1;
+}
+
+// One step: the MFMAs of step s with A from the LDS tile and B converted
+// from this step's raw chunks (Rc) just ahead of the MFMAs of the first row
+// tile that use it, interleaved with the conversion of step s + 1's A
+// chunks (Rn) into the other LDS tile. A wavefront issues one instruction
+// every few clocks while an MFMA keeps the matrix core busy for 32, so each
+// MFMA is followed by a share of the conversion units (8 elements each) and,
+// in the two-group kernels, scheduling fences keep that order (measured: with
+// one K group the compiler's own order is 4 % faster at 128 tokens x 384
+// experts; with two groups the fences win). The A fragments of row tile
+// rt + 1 are read right after their last use in row tile rt.
+template <int BM, int NTW>
+__device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& Rc, const _Float16* abuf, const MmaRegs<BM, NTW>& Rn,
+                                         _Float16* abuf_n, int lane,
+                                         f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
+  constexpr int NS = mma_sets<BM, NTW>();
+  constexpr int SL = mma_row_slots<BM>();
+  constexpr int NM = (BM / 32) * 8 * NTW;  // MFMAs; the first 8 NTW use B units 0 .. 8 NTW - 1 in order
+  constexpr int NB = 8 * NTW;              // B units
+  constexpr int NA = 4 * SL;               // A units
+  const int r = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x & (kMmaThreads - 1), q4 = tid & 3;
+  _Float16 bsc[NTW][2][2], asc[SL][2];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bsc[t][c][0] = e4m3_f16(Rc.bs[t][c] & 0xFFu);
+      bsc[t][c][1] = e4m3_f16(Rc.bs[t][c] >> 8);
+    }
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    asc[i][0] = e4m3_f16(Rn.as[i] & 0xFFu);
+    asc[i][1] = e4m3_f16(Rn.as[i] >> 8);
+  }
+  half8_t B[NTW][8];
+  // B unit m feeds MFMA m of the first row tile: K slice j = m / NTW of
+  // expert tile t = m % NTW.
+  auto bunit = [&](auto uc) {
+    constexpr int m = decltype(uc)::value, j = m / NTW, t = m % NTW;
+    B[t][j] = fp4x8_to_f16(Rc.b[t][j / 4][j % 4], bsc[t][j / 4][(j % 4) >> 1]);
+  };
+  auto aunit = [&](auto uc) {
+    constexpr int i = decltype(uc)::value / 4, q = decltype(uc)::value % 4;
+    const int row = (tid >> 2) + 64 * i;
+    if (BM >= 64 || row < BM)  // BM = 32: threads 128..255 hold no row
+      reinterpret_cast<half8_t*>(abuf_n + row * kMmaARow + 32 * q4)[q] = fp4x8_to_f16(Rn.a[i][q], asc[i][q >> 1]);
+  };
+  const _Float16* arow = abuf + r * kMmaARow + 32 * h;
+  auto afrag = [&](int rt, int j) {
+    return *reinterpret_cast<const half8_t*>(arow + rt * 32 * kMmaARow + (j < 4 ? 8 * j : 64 + 8 * (j - 4)));
+  };
+  half8_t A[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) A[j] = afrag(0, j);
+  bunit(IntC<0>{});
+  static_for<0, NM>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    constexpr int rt = m / (8 * NTW), j = (m / NTW) % 8, t = m % NTW;
+    f32x16_t& c = acc[NS == 2 ? (j >> 2) : 0][rt][t];
+    c = mfma32(A[j], B[t][j], c);
+    if constexpr (t == NTW - 1 && rt + 1 < BM / 32) A[j] = afrag(rt + 1, j);
+    if constexpr (m + 1 < NB) bunit(IntC<m + 1>{});
+    static_for<(m * NA + NM - 1) / NM, ((m + 1) * NA + NM - 1) / NM>(aunit);
+    if constexpr (mma_ksplit<BM, NTW>() == 2) __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+
+// The K loop of one workgroup tile: KS K groups of four wavefronts (group
+// grp takes K steps grp, grp + KS, ...), loads RING steps ahead in a register
+// ring, A converted into the group's two LDS tiles (abuf + (2 grp + i) BM
+// kMmaARow halves), B converted in registers. nsteps is padded to a multiple
+// of KS times the ring depth; padding steps load nothing (k >= D) and add
+// zeros. Leaves acc[0] holding this group's sums (the two accumulator sets
+// added).
+template <int BM, int NTW, int KS>
+__device__ __forceinline__ void mma_mainloop(const MmaPtrs<BM, NTW>& P, int D, int nsteps, _Float16* abuf_base,
+                                             int lane, f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
+  constexpr int NS = mma_sets<BM, NTW>();
+  const int grp = (threadIdx.x >> 6) >> 2;
+  auto abuf = [&](int i) { return abuf_base + (2 * grp + i) * (BM * kMmaARow); };
+#pragma unroll
+  for (int q = 0; q < NS; ++q)
+#pragma unroll
+    for (int rt = 0; rt < BM / 32; ++rt)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[q][rt][t][v] = 0.0f;
+  constexpr int RING = mma_ring<BM, NTW>();
+  MmaRegs<BM, NTW> R[RING];
+#pragma unroll
+  for (int p = 0; p < RING; ++p) mma_load<BM, NTW>(R[p], P, D, KS * p + grp);
+  mma_store_a<BM, NTW>(R[0], abuf(0));
+  __syncthreads();
+  for (int s0 = 0; s0 < nsteps; s0 += KS * RING) {
+    // The A tiles alternate with this group's step count, RING it + p: with
+    // an odd ring the parity of p alone does not alternate across passes.
+    const int par = (RING & 1) ? (s0 / (KS * RING)) & 1 : 0;
+#pragma unroll
+    for (int p = 0; p < RING; ++p) {
+      // Step s0 + KS p + grp: A from tile (p + par) & 1, B from R[p]; the
+      // next step's A (R[(p + 1) % RING]) into the other tile; then R[p]
+      // (fully used) reloads the step RING ahead.
+      mma_step<BM, NTW>(R[p], abuf((p + par) & 1), R[(p + 1) % RING], abuf((p + 1 + par) & 1), lane, acc);
+      mma_load<BM, NTW>(R[p], P, D, s0 + KS * (p + RING) + grp);
+      __syncthreads();
+    }
+  }
+  if (NS == 2) {
+#pragma unroll
+    for (int rt = 0; rt < BM / 32; ++rt)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) acc[0][rt][t] += acc[NS - 1][rt][t];
+  }
+}
+
+// K steps of 128 elements for D, padded to a multiple of KS times the ring depth.
+template <int BM, int NTW>
+inline int mma_padded_steps(int64_t D) {
+  constexpr int G = mma_ksplit<BM, NTW>() * mma_ring<BM, NTW>();
+  const int steps = (int)((D + 127) / 128);
+  return (steps + G - 1) / G * G;
+}
+
+}  // namespace nvr

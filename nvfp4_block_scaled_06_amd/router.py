@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4_router.so")
 ROUTER_OK = 0
 EXPORTS = ("router_workspace_bytes", "router_workspace_init", "router_quantize", "router_gate_topk",
            "router_forward", "router_forward_noalloc", "router_status_string", "router_probe_read",
-           "router_probe_mfma", "lmhead_workspace_bytes", "lmhead_argmax")
+           "router_probe_mfma", "lmhead_workspace_bytes", "lmhead_argmax", "grouped_offsets", "grouped_gemm")
 ROUTER_ESCRATCH = -4
 STATIC_SCRATCH_BYTES = 16 << 20
 
@@ -62,6 +62,10 @@ def load_library(path=LIB_PATH):
     L.lmhead_workspace_bytes.restype = sz
     L.lmhead_argmax.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     L.lmhead_argmax.restype = ctypes.c_int
+    L.grouped_offsets.argtypes = [vp, i64, i64, vp, vp]
+    L.grouped_offsets.restype = ctypes.c_int
+    L.grouped_gemm.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp]
+    L.grouped_gemm.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -259,6 +263,68 @@ def lmhead_argmax(xq, wq, workspace, want_logits=False):
                                         _ptr(wq.scales), _ptr(wq.gscale), T, D, N, _ptr(idx), _ptr(logit),
                                         _ptr(logits), _ptr(workspace.buf), workspace.nbytes, _stream()))
     return idx, logit, logits
+
+
+class GroupedWeights:
+    """NVFP4 weights of G groups: codes [G, N, D/2], scales [G, N, D/16], global scales [G] (one per group)."""
+
+    def __init__(self, codes, scales, gscale):
+        self.codes, self.scales, self.gscale = codes, scales, gscale
+
+    @property
+    def G(self):
+        return self.codes.shape[0]
+
+    @property
+    def N(self):
+        return self.codes.shape[1]
+
+    @property
+    def D(self):
+        return self.codes.shape[2] * 2
+
+
+def quantize_grouped_weights(w, workspace):
+    """Each group's bf16 weight [G, N, D] quantized with its own global scale (router_quantize per group, at
+    load time) into one GroupedWeights."""
+    _device_tensor(w, "w", (torch.bfloat16, torch.int16, torch.uint16), ndim=3)
+    G, N, D = w.shape
+    dev = w.device
+    out = GroupedWeights(torch.empty((G, N, D // 2), dtype=torch.uint8, device=dev),
+                         torch.empty((G, N, D // 16), dtype=torch.uint8, device=dev),
+                         torch.empty(G, dtype=torch.float32, device=dev))
+    for g in range(G):
+        quantize(w[g], workspace, out=NVFP4Tensor(out.codes[g], out.scales[g], out.gscale[g:g + 1]))
+    return out
+
+
+def grouped_offsets(range_buf, padded_rows, out=None):
+    """grouped_offsets: offsets [G + 1] int32 = range_buf * padded_rows on the device."""
+    _device_tensor(range_buf, "range_buf", (torch.int32,), ndim=1)
+    G = range_buf.numel() - 1
+    if out is None:
+        out = torch.empty(G + 1, dtype=torch.int32, device=range_buf.device)
+    _check(load_library().grouped_offsets(_ptr(range_buf), G, int(padded_rows), _ptr(out), _stream()))
+    return out
+
+
+def grouped_gemm(xq, wg, offsets, max_rows, out=None):
+    """grouped_gemm: out [R, N] fp32 with out[r] = gsa * gsw[g] * xhat[r] . what_g^T for the rows of group g."""
+    R, D = xq.rows, xq.D
+    for name, t in (("x codes", xq.codes), ("x scales", xq.scales)):
+        _device_tensor(t, name, (torch.uint8,), ndim=2)
+    for name, t in (("w codes", wg.codes), ("w scales", wg.scales)):
+        _device_tensor(t, name, (torch.uint8,), ndim=3)
+    _device_tensor(wg.gscale, "w scales", (torch.float32,), ndim=1)
+    _device_tensor(offsets, "offsets", (torch.int32,), ndim=1)
+    if wg.D != D or offsets.numel() != wg.G + 1:
+        raise RouterError("grouped weights / offsets do not match x")
+    if out is None:
+        out = torch.empty((R, wg.N), dtype=torch.float32, device=xq.codes.device)
+    _check(load_library().grouped_gemm(_ptr(xq.codes), _ptr(xq.scales), _ptr(xq.gscale), _ptr(wg.codes),
+                                       _ptr(wg.scales), _ptr(wg.gscale), _ptr(offsets), wg.G, R, int(max_rows),
+                                       wg.N, D, _ptr(out), _stream()))
+    return out
 
 
 MFMA_PROBE_SINK = 1024 * 256

@@ -21,7 +21,8 @@ cfg   name            T      D     E    k   r    structure
 5     large_prefill   32768  7168  384  8   2.5  x ~ Student-t(4); bias ~ U(-0.05, 0.05)
 ====  ==============  =====  ====  ===  ==  ===  ====================================
 
-Gate weights are bf16 N(0, 0.02^2) in every config.
+Gate weights are bf16 N(0, 0.02^2) in every config. Grouped-layer shapes
+(configs 11..13) are listed in GROUPED_CONFIGS.
 """
 
 from dataclasses import dataclass
@@ -103,6 +104,43 @@ def make_bias(cfg, layer=0):
     c = CONFIGS[cfg]
     h = c.bias_half_width
     return rng(cfg, 2, layer).uniform(-h, h, size=c.E).astype(np.float32)
+
+
+@dataclass(frozen=True)
+class GroupedConfig:
+    """A grouped linear layer: G groups of padded_rows rows each (flattened to [G * P, D]) and G weights
+    [N, D], one per group."""
+    cfg: int
+    name: str
+    G: int
+    P: int
+    D: int
+    N: int
+
+
+# Grouped layers (the step after the router: the routed experts' projections). No sizes are given for them, so
+# these take a DeepSeek-V3-shaped expert: D = 7168 in, N = 4096 out (the gate and up projections of a
+# 2048-wide expert side by side), G = 8 groups (the k = 8 experts a token is routed to). Decode: one row per
+# group; prefill: 1024 rows per group (8192 routed rows).
+GROUPED_CONFIGS = {
+    11: GroupedConfig(11, "grouped_tiny", 3, 5, 256, 48),
+    12: GroupedConfig(12, "grouped_decode", 8, 1, 7168, 4096),
+    13: GroupedConfig(13, "grouped_prefill", 8, 1024, 7168, 4096),
+}
+
+
+def make_grouped_x(gcfg):
+    """Flattened activations [G * P, D] bf16: N(0,1) rows times a LogNormal(0, 0.5) magnitude per row."""
+    c = GROUPED_CONFIGS[gcfg]
+    a = rng(gcfg, 0).standard_normal((c.G * c.P, c.D), dtype=np.float32)
+    a *= rng(gcfg, 4).lognormal(0.0, 0.5, size=c.G * c.P).astype(np.float32)[:, None]
+    return bf16_bits(a)
+
+
+def make_grouped_w(gcfg, g):
+    """Group g's weight [N, D] bf16 ~ N(0, 0.02^2)."""
+    c = GROUPED_CONFIGS[gcfg]
+    return bf16_bits(rng(gcfg, 1, g).standard_normal((c.N, c.D), dtype=np.float32) * np.float32(W_STD))
 
 
 def sample_rows(T, n, seed=0):

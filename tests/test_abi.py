@@ -147,3 +147,26 @@ def test_noalloc_rejects_sizes_beyond_its_static_scratch(lib):
     assert lib.router_forward_noalloc(*bad) == -1
     bad = list(args); bad[1] = 1; bad[12] = 600  # E > 512
     assert lib.router_forward_noalloc(*bad) == -2
+
+
+def test_grouped_entry_points_reject_bad_arguments(lib):
+    p = ctypes.c_void_p(0x100000)
+    assert lib.grouped_offsets(p, 0, 4, p, None) == -1  # G >= 1
+    assert lib.grouped_offsets(p, 8, -1, p, None) == -1
+    assert lib.grouped_offsets(None, 8, 4, p, None) == -1
+    assert lib.grouped_offsets(p, 1 << 20, 1 << 12, p, None) == -1  # G * padded_rows >= 2^31
+    args = [p, p, p, p, p, p, p, 8, 8, 1, 4096, 7168, p, None]
+
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return lib.grouped_gemm(*a)
+
+    assert call(7, 0) == -1  # G
+    assert call(11, 7176) == -1  # D % 16
+    assert call(11, 7184) == -2  # D % 32: the MFMA tiles read 32-element chunks
+    assert call(6, None) == -1  # offsets
+    assert call(0, ctypes.c_void_p(0x100008)) == -1  # x codes not 16-byte aligned
+    assert call(10, 0) == -1  # N
+    assert call(8, 0) == 0  # no rows: nothing to do
+    assert call(9, 0) == 0  # no rows per group: nothing to do

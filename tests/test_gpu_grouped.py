@@ -1,0 +1,227 @@
+"""GPU parity of the grouped NVFP4 GEMM (grouped_offsets, router_quantize over the flattened groups,
+grouped_gemm) against the CPU oracle, through the C ABI.
+
+Quantized bytes and scales must match bit for bit; outputs within 1e-5 of the |x||w| scale A, and within a
+plain relative 1e-5 on the outputs at or above their row's median magnitude. Small shapes are compared in full;
+the decode-size layer (8 groups x 4096 x 7168) on every row and 256 sampled columns per group, the prefill-size
+layer (8 x 1024 rows) on rows at every tile boundary plus random rows, and sampled columns.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import bf16_exact, load_golden
+from nvfp4_block_scaled_06_amd import router as rt
+from nvfp4_block_scaled_06_amd import workloads as wl
+from oracle import check, quant_ref
+from oracle.grouped_ref import grouped_products, grouped_ref, offsets_ref
+
+pytestmark = pytest.mark.gpu
+
+PLAIN_REL_BOUND = 1e-5
+
+
+def log(msg):
+    print(f"[gpu-grouped] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rt.load_library()
+    d = torch.device("cuda:0")
+    torch.cuda.set_device(d)
+    return d
+
+
+@pytest.fixture(scope="module")
+def ws(dev):
+    return rt.Workspace(rt.workspace_bytes(8192, 7168, 256, 8), dev)
+
+
+def to_dev(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+
+
+def run_grouped(dev, ws, x_bits, w_bits, offsets, max_rows, fill=np.nan):
+    """router_quantize over the flattened rows, per-group weight quantization, then grouped_gemm into an output
+    pre-filled with `fill` (rows of no group must keep it)."""
+    xq = rt.quantize(to_dev(x_bits, dev), ws)
+    wg = rt.quantize_grouped_weights(to_dev(w_bits, dev), ws)
+    off = torch.tensor(np.asarray(offsets, dtype=np.int32), device=dev)
+    out = torch.full((x_bits.shape[0], w_bits.shape[1]), fill, dtype=torch.float32, device=dev)
+    rt.grouped_gemm(xq, wg, off, max_rows, out=out)
+    torch.cuda.synchronize()
+    return xq, wg, out.cpu().numpy()
+
+
+def host_q(q):
+    return q.codes.cpu().numpy(), q.scales.cpu().numpy(), q.gscale.cpu().numpy()
+
+
+def assert_outputs(Y, ref_Y, ref_A, what):
+    fails = check.check_logits(Y, ref_Y, ref_A)
+    assert not fails, f"{what}:\n" + "\n".join(fails)
+    ra, rel = check.logit_error_stats(Y, ref_Y, ref_A)
+    log(f"{what}: max |dY|/A = {ra:.3g}, max rel err (|Y| >= median) = {rel:.3g}")
+    assert rel <= PLAIN_REL_BOUND, f"{what}: plain relative error {rel:.3g}"
+
+
+def test_offsets_on_the_device(dev):
+    for G, P in ((1, 0), (4, 3), (8, 1), (8, 1024), (1000, 7)):
+        rng_buf = torch.arange(G + 1, dtype=torch.int32, device=dev)
+        off = rt.grouped_offsets(rng_buf, P)
+        torch.cuda.synchronize()
+        assert off.cpu().numpy().tolist() == offsets_ref(G, P).tolist(), (G, P)
+
+
+@pytest.mark.parametrize("name", ["per_group_weight_scale", "shared_activation_scale"])
+def test_hand_cases(dev, ws, name):
+    c = load_golden("grouped_worked_examples.json")[name]
+    # The cases have D = 16; the MFMA tiles take D % 32 == 0, so a zero block is appended (it changes neither
+    # the global scales nor any product).
+    x = np.stack([bf16_exact(r) for r in c["x"]])
+    w = np.stack([np.stack([bf16_exact(r) for r in wg]) for wg in c["w"]])
+    x = np.concatenate([x, np.zeros_like(x)], axis=-1)
+    w = np.concatenate([w, np.zeros_like(w)], axis=-1)
+    log(f"hand case {name}")
+    xq, wg, Y = run_grouped(dev, ws, x, w, c["offsets"], 1)
+    assert Y.tolist() == c["expect_Y"]
+    if "expect_gsw" in c:
+        assert wg.gscale.cpu().numpy().tolist() == c["expect_gsw"]
+    if "expect_gsa" in c:
+        assert float(xq.gscale.cpu()[0]) == c["expect_gsa"]
+        assert xq.scales.cpu().numpy()[:, 0].tolist() == [int(h, 16) for h in c["expect_scales_hex"]]
+
+
+def synth(shape, seed, scale=1.0):
+    return wl.bf16_bits((np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32))
+
+
+@pytest.mark.parametrize("G,P,D,N", [
+    (3, 5, 256, 48),       # the tiny layer: 32-row tiles, ragged columns
+    (2, 1, 7168, 300),     # decode-size rows, columns past a 128 tile
+    (4, 33, 512, 130),     # 64-row tiles with a ragged last row tile, ragged columns
+    (2, 100, 1024, 256),   # 128-row tiles, ragged rows
+    (3, 200, 2048, 520),   # 128-row tiles, wider column tiles, ragged columns
+    (1, 64, 256, 128),     # one group, exactly one tile
+    (5, 2, 1056, 40),      # D not a multiple of 128
+])
+def test_grouped_shapes(dev, ws, G, P, D, N):
+    log(f"grouped G={G} P={P} D={D} N={N}")
+    x = synth((G * P, D), G * 100 + P)
+    # Different magnitudes per group (powers of two, exact in bf16): each group gets its own weight scale.
+    w = wl.bf16_bits(wl.bf16_to_f32(synth((G, N, D), D + N, 0.02)) *
+                     (np.float32(2.0) ** np.arange(G, dtype=np.float32))[:, None, None])
+    offsets = offsets_ref(G, P)
+    xq, wg, Y = run_grouped(dev, ws, x, w, offsets, P)
+    ref = grouped_ref(x, offsets, w)
+    fails = check.check_quant(*host_q(xq), ref["xq"])
+    for g in range(G):
+        fails += check.check_quant(wg.codes[g].cpu().numpy(), wg.scales[g].cpu().numpy(),
+                                   wg.gscale[g:g + 1].cpu().numpy(), ref["wq"][g])
+    assert not fails, "\n".join(fails)
+    assert_outputs(Y, ref["Y"], ref["A"], f"G={G} P={P} D={D} N={N}")
+
+
+def test_general_offsets_with_an_empty_group(dev, ws):
+    """Offsets that are not a multiple of one padded size, a group with no rows, and rows of no group (their
+    output rows stay untouched)."""
+    offsets = [0, 3, 3, 40]
+    G, R, D, N = 3, 45, 512, 70
+    x = synth((R, D), 77)
+    w = synth((G, N, D), 78, 0.02)
+    log("general offsets [0, 3, 3, 40], 45 rows")
+    xq, wg, Y = run_grouped(dev, ws, x, w, offsets, 37, fill=-123.0)
+    ref = grouped_ref(x, offsets, w)
+    assert_outputs(Y[:40], ref["Y"][:40], ref["A"][:40], "general offsets")
+    assert np.all(Y[40:] == -123.0)
+
+
+def test_bound_on_rows_per_group(dev, ws):
+    """Rows of a group past max_rows are not computed (the caller's bound sizes the grid)."""
+    G, P, D, N = 2, 40, 256, 64
+    x = synth((G * P, D), 5)
+    w = synth((G, N, D), 6, 0.02)
+    log("max_rows smaller than the groups")
+    _, _, Y = run_grouped(dev, ws, x, w, offsets_ref(G, P), 32, fill=-7.0)
+    ref = grouped_ref(x, offsets_ref(G, P), w)
+    for g in range(G):
+        rows = slice(g * P, g * P + 32)
+        assert_outputs(Y[rows], ref["Y"][rows], ref["A"][rows], f"group {g}, first 32 rows")
+        assert np.all(Y[g * P + 32:(g + 1) * P] == -7.0)
+
+
+def full_size_case(dev, ws, gcfg, rows):
+    """A full-size layer on the GPU, checked on `rows` (all columns' quantization in full, products on 256
+    sampled columns per group) against the oracle under the whole tensors' global scales."""
+    c = wl.GROUPED_CONFIGS[gcfg]
+    x = wl.make_grouped_x(gcfg)
+    w = np.stack([wl.make_grouped_w(gcfg, g) for g in range(c.G)])
+    offsets = offsets_ref(c.G, c.P)
+    log(f"full size {c.name}: G={c.G} P={c.P} D={c.D} N={c.N}")
+    xq, wg, Y = run_grouped(dev, ws, x, w, offsets, c.P)
+    gsa = quant_ref.gsa_ref(max(quant_ref.amax_ref(x[i:i + 2048]) for i in range(0, x.shape[0], 2048)))
+    xr = quant_ref.quantize_ref(x[rows], gsa_override=gsa)
+    codes, scales, g_dev = host_q(xq)
+    fails = check.check_quant(codes[rows], scales[rows], g_dev, xr)
+    cols = np.unique(np.concatenate([[0, 127, 128, c.N - 1],
+                                     np.random.default_rng(gcfg).choice(c.N, 252, replace=False)]))
+    wq_cols = []
+    for g in range(c.G):
+        gsw = quant_ref.gsa_ref(quant_ref.amax_ref(w[g]))
+        wq_cols.append(quant_ref.quantize_ref(w[g][cols], gsa_override=gsw))
+        ci = torch.from_numpy(cols).to(dev)
+        fails += check.check_quant(wg.codes[g][ci].cpu().numpy(), wg.scales[g][ci].cpu().numpy(),
+                                   wg.gscale[g:g + 1].cpu().numpy(), wq_cols[-1])
+    assert not fails, "\n".join(fails[:20])
+    ref = grouped_products(xr, wq_cols, offsets, rows=rows)
+    assert_outputs(Y[rows][:, cols], ref["Y"], ref["A"], f"{c.name}, {len(rows)} rows x {len(cols)} columns")
+
+
+def test_full_size_decode(dev, ws):
+    c = wl.GROUPED_CONFIGS[12]
+    full_size_case(dev, ws, 12, np.arange(c.G * c.P))
+
+
+def test_full_size_prefill(dev, ws):
+    c = wl.GROUPED_CONFIGS[13]
+    edges = [g * c.P + r for g in range(c.G) for r in (0, 1, 63, 64, 127, 128, 511, 512, c.P - 1)]
+    extra = np.random.default_rng(13).choice(c.G * c.P, 64, replace=False)
+    full_size_case(dev, ws, 13, np.unique(np.concatenate([edges, extra])))
+
+
+def test_graph_capture_replays_match_eager(dev, ws):
+    """Offsets, the flattened quantize and the grouped GEMM captured in one graph and replayed."""
+    c = wl.GROUPED_CONFIGS[11]
+    x = to_dev(wl.make_grouped_x(11), dev)
+    wg = rt.quantize_grouped_weights(to_dev(np.stack([wl.make_grouped_w(11, g) for g in range(c.G)]), dev), ws)
+    rng_buf = torch.arange(c.G + 1, dtype=torch.int32, device=dev)
+    off = torch.empty(c.G + 1, dtype=torch.int32, device=dev)
+    xq = rt.empty_nvfp4(c.G * c.P, c.D, dev)
+    out = torch.empty((c.G * c.P, c.N), dtype=torch.float32, device=dev)
+
+    def step():
+        rt.grouped_offsets(rng_buf, c.P, out=off)
+        rt.quantize(x, ws, out=xq)
+        rt.grouped_gemm(xq, wg, off, c.P, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    log("graph capture of the grouped layer")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        out.zero_()
+        off.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
