@@ -5,6 +5,7 @@
 #include "../../include/nvfp4_router.h"
 #include "router_internal.hpp"
 
+#include <algorithm>
 #include <mutex>
 
 static_assert(nvr::kScratchOffset == ROUTER_WORKSPACE_STATE_BYTES, "the documented zero-state prefix");
@@ -49,6 +50,7 @@ size_t router_workspace_bytes(int64_t T, int64_t D, int64_t E, int64_t k) {
   size_t scratch = nvr::quantize_scratch_bytes();
   const size_t g = nvr::gate_scratch_bytes(T, D, E);
   if (g > scratch) scratch = g;
+  if (nvr::batch_fits(T, D)) scratch = std::max(scratch, nvr::batch_scratch_bytes(T, D, E));
   return nvr::kScratchOffset + scratch;
 }
 
@@ -125,6 +127,13 @@ int router_forward(const void* x, int64_t T, int64_t D, const float* gsa_overrid
   if (qneed > 0 && (!workspace || workspace_bytes < qneed || !aligned(workspace, 256))) return ROUTER_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
+  if (T > 0 && nvr::batch_fits(T, D)) {
+    const size_t need = nvr::kScratchOffset + nvr::batch_scratch_bytes(T, D, E);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return ROUTER_EINVAL;
+    return status_from(nvr::launch_forward_batch(x, gsa_override, x_codes, x_scales, gsa_out, w_codes, w_scales, gsw,
+                                                 bias, routed_scale, T, D, E, k, topk_idx, topk_w, logits_out,
+                                                 base + nvr::kScratchOffset, s));
+  }
   if (T > 0 && nvr::forward_single_launch(T, D)) {
     return status_from(nvr::launch_forward_fused(x, gsa_override, x_codes, x_scales, gsa_out, w_codes, w_scales, gsw,
                                                  bias, routed_scale, T, D, E, k, topk_idx, topk_w, logits_out, base,

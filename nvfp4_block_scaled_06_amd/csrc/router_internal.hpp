@@ -19,8 +19,9 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 //                          clears it), and written by no other kernel;
 //   [kScratchOffset, ...)  per-call scratch (partial maxima of the quantizer,
 //                          the [T, E] logits of the tile gate and of the
-//                          split-expert prefill gate, the lm_head's
-//                          per-workgroup candidates).
+//                          split-expert prefill gate, the batched-decode
+//                          forward's partial maxima and flagged slice
+//                          partials, the lm_head's per-workgroup candidates).
 constexpr size_t kCounterBytes = 4096;
 constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(uint32_t));
 constexpr size_t kDecodeRegionOffset = kCounterBytes;
@@ -72,6 +73,18 @@ hipError_t launch_forward_fused(const void* x, const float* gsa_override, uint8_
                                 float* gsa_out, const uint8_t* w_codes, const uint8_t* w_scales, const float* gsw,
                                 const float* bias, float routed_scale, int64_t T, int64_t D, int64_t E, int64_t k,
                                 int32_t* topk_idx, float* topk_w, float* logits_out, void* workspace,
+                                hipStream_t stream);
+
+// Batched-decode forward (gate_batch.hip; router_forward only): 4 < T <= 256
+// and D <= 16384, in two launches. Its per-call scratch (partial maxima, then
+// the flagged slice partials, batch_scratch_bytes in all) starts at
+// kScratchOffset.
+bool batch_fits(int64_t T, int64_t D);
+size_t batch_scratch_bytes(int64_t T, int64_t D, int64_t E);
+hipError_t launch_forward_batch(const void* x, const float* gsa_override, uint8_t* x_codes, uint8_t* x_scales,
+                                float* gsa_out, const uint8_t* w_codes, const uint8_t* w_scales, const float* gsw,
+                                const float* bias, float routed_scale, int64_t T, int64_t D, int64_t E, int64_t k,
+                                int32_t* topk_idx, float* topk_w, float* logits_out, void* scratch,
                                 hipStream_t stream);
 
 }  // namespace nvr

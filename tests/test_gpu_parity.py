@@ -459,10 +459,20 @@ def test_graph_capture_replays_match_eager(dev, ws, cfg):
                                          (None, 2, 7168, 100, 8),    # single launch, E not a multiple of 16
                                          (None, 3, 4128, 256, 8),    # single launch, ragged last K slice
                                          (None, 4, 4128, 100, 5),    # both
-                                         (3, 64, 7168, 256, 8)])     # batched decode (timed by the benchmark)
+                                         (3, 64, 7168, 256, 8),      # batched decode (timed by the benchmark)
+                                         (None, 5, 7168, 256, 8),    # smallest batched-decode T
+                                         (None, 17, 4128, 100, 6),   # batched: ragged rows, last slice, experts
+                                         (None, 8, 32, 16, 1),       # batched: one K step, one expert tile, top-1
+                                         (None, 40, 1056, 64, 4),    # batched: second slice two blocks
+                                         (None, 64, 7168, 300, 8),   # batched: ragged last expert quarter
+                                         (None, 255, 2048, 512, 32),  # batched: largest E and k, ragged rows
+                                         (None, 256, 16384, 256, 8),  # batched: largest T and D
+                                         (None, 100, 16416, 64, 4),  # D past the batched path: two-call path
+                                         (None, 257, 1024, 256, 8)])  # T past the batched path
 @pytest.mark.parametrize("want_logits", [True, False], ids=["logits", "nologits"])
 def test_forward_matches_oracle(dev, ws, cfg, T, D, E, k, want_logits):
-    """router_forward (single launch at decode sizes) gives the quantizer's bytes and the oracle's routing."""
+    """router_forward (one launch at T <= 4, two fused launches up to T = 256) gives the quantizer's bytes and the
+    oracle's routing."""
     if cfg is not None:
         x, w, bias = wl.make_x(cfg), wl.make_w(cfg), wl.make_bias(cfg)
         r = wl.CONFIGS[cfg].routed_scale
@@ -481,9 +491,10 @@ def test_forward_matches_oracle(dev, ws, cfg, T, D, E, k, want_logits):
                  f"forward T={T}")
 
 
-def test_forward_static_scale_override(dev, ws):
-    c = wl.CONFIGS[2]
-    x, w, bias = wl.make_x(2, 3), wl.make_w(2, 3), wl.make_bias(2, 3)
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_forward_static_scale_override(dev, ws, cfg):
+    c = wl.CONFIGS[cfg]
+    x, w, bias = wl.make_x(cfg, 3), wl.make_w(cfg, 3), wl.make_bias(cfg, 3)
     ov = float(quant_ref.gsa_ref(quant_ref.amax_ref(x))) / 4
     log("forward with gsa override")
     wq = gpu_quant(w, dev, ws)
@@ -496,17 +507,18 @@ def test_forward_static_scale_override(dev, ws):
     assert_route(ref, idx.cpu().numpy(), wts.cpu().numpy(), logits.cpu().numpy(), c.k, c.routed_scale, "override")
 
 
-def test_forward_graph_replay_cycles_layers(dev, ws):
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_forward_graph_replay_cycles_layers(dev, ws, cfg):
     """Decode loop as the benchmark runs it: several layer sets captured in one graph, replayed twice."""
-    c = wl.CONFIGS[2]
+    c = wl.CONFIGS[cfg]
     L = 5
-    xs = [to_dev(wl.make_x(2, l), dev) for l in range(L)]
-    wqs = [gpu_quant(wl.make_w(2, l), dev, ws) for l in range(L)]
-    bs = [torch.from_numpy(wl.make_bias(2, l)).to(dev) for l in range(L)]
-    xq = [rt.empty_nvfp4(1, c.D, dev) for _ in range(L)]
-    outs = [(torch.empty((1, c.k), dtype=torch.int32, device=dev), torch.empty((1, c.k), dtype=torch.float32, device=dev),
-             None) for _ in range(L)]
-    log("forward graph replay")
+    xs = [to_dev(wl.make_x(cfg, l), dev) for l in range(L)]
+    wqs = [gpu_quant(wl.make_w(cfg, l), dev, ws) for l in range(L)]
+    bs = [torch.from_numpy(wl.make_bias(cfg, l)).to(dev) for l in range(L)]
+    xq = [rt.empty_nvfp4(c.T, c.D, dev) for _ in range(L)]
+    outs = [(torch.empty((c.T, c.k), dtype=torch.int32, device=dev),
+             torch.empty((c.T, c.k), dtype=torch.float32, device=dev), None) for _ in range(L)]
+    log(f"forward graph replay cfg {cfg}")
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -523,7 +535,8 @@ def test_forward_graph_replay_cycles_layers(dev, ws):
         g.replay()
         torch.cuda.synchronize()
         for l in range(L):
-            ref = router_ref.router_ref(wl.make_x(2, l), wl.make_w(2, l), wl.make_bias(2, l), c.k, c.routed_scale)
+            ref = router_ref.router_ref(wl.make_x(cfg, l), wl.make_w(cfg, l), wl.make_bias(cfg, l), c.k,
+                                        c.routed_scale)
             fails = check.check_topk(outs[l][0].cpu().numpy(), outs[l][1].cpu().numpy(), ref["s"], ref["b"], c.k,
                                      c.routed_scale)
             assert not fails, f"replay {rep} layer {l}: " + "; ".join(fails)
