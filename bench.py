@@ -85,11 +85,6 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def gate_bytes(c):
-    """Algorithmic bytes of one gate launch: W codes+scales, x codes+scales, bias, outputs."""
-    return c.E * c.D * 9 // 16 + c.T * c.D * 9 // 16 + 4 * c.E + 8 * c.T * c.k
-
-
 def quant_bytes(c):
     """Algorithmic bytes of one quantize call: x read once (single pass) or twice, codes+scales written."""
     reads = 2 if c.T * c.D // 16 > 2048 else 1
@@ -588,11 +583,18 @@ def main():
         roof = rb.prefill_roofline(r)
     elif c.T > 4:
         # Batched decode: a few hundred MFLOP against a megabyte of weights; bytes bound it (in practice the
-        # loads' and the handoff's latency).
-        achieved = gate_bytes(c) / r["tg"] / 1e9
+        # loads' and the handoff's latency). router_forward is two launches here (the amax pass, then the
+        # fused quantize + gate + route kernel); the events around the timed replay give the call's duration,
+        # both launches and the gap between them included.
+        nbytes = forward_bytes(c)
+        t_call = r["tf"] if r["ev_fwd"] is None else r["ev_fwd"] / K
+        achieved = nbytes / t_call / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gate_tile_kernel",
-                "algorithmic": f"{gate_bytes(c)} B per launch"}
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "batch_amax_zero_kernel + gate_batch_kernel (router_forward: two launches)",
+                "launch_us": t_call * 1e6,
+                "algorithmic": f"{nbytes} B per call",
+                "probe": probe_rates(torch, rt, c, nbytes, rb.time_graph, K, t_call, args.eager)}
     else:
         # One launch per step: the events around the timed replay give the average launch duration.
         nbytes = forward_bytes(c)
