@@ -73,7 +73,7 @@ extern "C" {
  * pre-allocate the output buffer and the expert-offset range buffer once at
  * initialization instead of per call).
  *
- * The first ROUTER_WORKSPACE_STATE_BYTES bytes (arrival counters and the
+ * The first ROUTER_WORKSPACE_STATE_BYTES bytes (arrival counters, then the
  * decode gate's flagged partials) must be zero before the first call
  * (allocate zero-filled memory or call router_workspace_init), and every call
  * leaves them zero again; the rest is per-call scratch. Every size this
@@ -152,11 +152,14 @@ int router_gate_topk(const uint8_t* x_codes, const uint8_t* x_scales, const floa
  * router_quantize followed by router_gate_topk, in one call and with the same
  * results: x_codes, x_scales and gsa_out are written exactly as
  * router_quantize writes them, and the routing is that of router_gate_topk on
- * them. For decode-size batches (T <= 4) it is a single kernel launch (the
- * single-launch fused router that commit 04cf8ca8, dsv4/layers/router.py,
- * gives priority over the two-launch path): every workgroup derives gsa from
- * all of x and quantizes the blocks it multiplies in registers. Larger T runs
- * the quantize kernels and then the gate kernels on the stream.
+ * them. For decode-size batches (T <= 4, D <= 16384) it is a single kernel
+ * launch (the single-launch fused router that commit 04cf8ca8,
+ * dsv4/layers/router.py, gives priority over the two-launch path): every
+ * workgroup derives gsa from all of x and quantizes the blocks it multiplies
+ * in registers. Batched decode (4 < T <= 256, D <= 16384) is two launches: a
+ * pass that takes the partial maxima of x, then one kernel that quantizes,
+ * multiplies and routes (each workgroup quantizes the x tile it multiplies).
+ * Larger T runs the quantize kernels and then the gate kernels.
  *
  * Arguments as in the two calls above: x [T, D] bf16 (16-byte aligned);
  * x_codes (16-byte aligned), x_scales and gsa_out are outputs; the size
@@ -181,7 +184,9 @@ int router_forward(const void* x, int64_t T, int64_t D, const float* gsa_overrid
  *
  * Calls whose router_workspace_bytes(T, D, E, k) exceeds 16 MiB (prefill
  * batches whose experts are split over workgroups with T * E * 4 above it,
- * e.g. T = 16384 at E = 256) return ROUTER_ESCRATCH before any launch;
+ * e.g. T = 16384 at E = 256; batched-decode calls whose slice partials,
+ * 4 * T * E * ceil(D / 256) bytes, exceed it, e.g. T = 256, D = 16384,
+ * E = 512) return ROUTER_ESCRATCH before any launch;
  * invalid or unsupported sizes give router_forward's status. Every call on one
  * GPU shares that GPU's array: calls that overlap in time on one GPU (other
  * streams, other threads) race and give wrong results; enqueue them in order.
