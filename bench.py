@@ -352,10 +352,12 @@ def grouped_bench(torch, gcfg, K, W):
     tk = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
     flops = 2 * R * c.N * c.D
     nbytes = c.G * c.N * c.D * 9 // 16 + 4 * c.G + R * c.D * 9 // 16 + 4 + 4 * (c.G + 1) + 4 * R * c.N
+    gemv = c.P <= 4 and c.P * c.D <= 32768 and c.D <= 16384  # grouped_gemm's decode-size (GEMV) path
     if c.P <= 4:
         achieved = nbytes / tk / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "grouped_mfma_kernel",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "grouped_gemv_kernel" if gemv else "grouped_mfma_kernel",
                 "kernel_launch_us": tk * 1e6, "algorithmic": f"{nbytes} B per launch"}
     else:
         achieved = flops / tk / 1e12
@@ -368,7 +370,8 @@ def grouped_bench(torch, gcfg, K, W):
         "metric": f"grouped NVFP4 layer rows/s, G={c.G} P={c.P} D={c.D} N={c.N}", "value": R / t, "unit": "rows/s",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": wall / K * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "nvfp4 operands, exact f16 products on 32x32x16 f16 MFMA, f32 accumulate", "data": "synthetic",
+        "dtype": ("nvfp4 operands, exact f16 products on the VALU (v_dot2), f32 accumulate" if gemv else
+                  "nvfp4 operands, exact f16 products on 32x32x16 f16 MFMA, f32 accumulate"), "data": "synthetic",
         "config": {"workload": f"{c.name} G={c.G} P={c.P} D={c.D} N={c.N}",
                    "entry": "grouped_offsets + router_quantize + grouped_gemm", "launch": "hipgraph",
                    "us_per_call": t * 1e6, "gemm_launch_us": tk * 1e6},

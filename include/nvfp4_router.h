@@ -273,7 +273,10 @@ int grouped_offsets(const int32_t* range, int64_t G, int64_t padded_rows, int32_
  * Code pointers 16-byte, scale pointers 2-byte, the rest 4-byte aligned.
  * ROUTER_EINVAL for bad sizes or pointers; ROUTER_EUNSUPPORTED for D % 32 !=
  * 0, D > ROUTER_MAX_GATE_D or a grid beyond 2^31 workgroups. One launch on
- * `stream`, no workspace, no host sync: capturable.
+ * `stream`, no workspace, no host sync: capturable. Decode-size groups
+ * (max_rows <= 4, max_rows * D <= 32768, D <= 16384) run as a stream of the
+ * weights with fp16 dot products on the VALU; larger groups on fp16 MFMA
+ * tiles. Both give exact products and fp32 sums in a fixed order.
  */
 int grouped_gemm(const uint8_t* x_codes, const uint8_t* x_scales, const float* gsa, const uint8_t* w_codes,
                  const uint8_t* w_scales, const float* gsw, const int32_t* offsets, int64_t G, int64_t R,

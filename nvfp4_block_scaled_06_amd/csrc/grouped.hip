@@ -14,8 +14,9 @@
 // from grouped_offsets, the element-wise product of a caller-allocated range
 // buffer with padded_rows.
 //
-// Workgroup (g, row tile, column tile): BM rows of group g times 128 NTW
-// weight rows, on the shared MFMA tile machinery (exact fp16 operands, fp32
+// Decode-size groups (at most 4 rows each) take a GEMV kernel (below); larger
+// groups take workgroup (g, row tile, column tile): BM rows of group g times
+// 128 NTW weight rows, on the shared MFMA tile machinery (exact fp16 operands, fp32
 // accumulation). Row tiles past a group's end exit at once; rows past it
 // inside a tile read zeros through the buffer descriptors and are not
 // stored. Epilogue: with two K groups, group 1 leaves its sums in LDS and
@@ -106,6 +107,104 @@ __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_e
     }
 }
 
+// Decode-size groups (at most kGvMaxRows rows per group): the layer is a
+// stream of the packed expert weights, so it takes the lm_head GEMV's
+// shape rather than MFMA tiles (which would multiply mostly zero rows).
+// Workgroup (g, column tile) = 64 weight rows of group g, four wavefronts
+// of 16 rows with 4 rows' loads in flight; lane l takes the 32-element
+// chunks l, l + 64, ... of a row (coalesced 1 KB per wavefront load,
+// nontemporal: every weight byte is read once). The group's rows of x are
+// converted once per workgroup into LDS as exact fp16 q S values; block
+// products are exact in fp32, per-lane sums and the wavefront sum run in a
+// fixed order, and the result is scaled by gsa * gsw[g] as in the tile path.
+constexpr int kGvWaves = 4;
+constexpr int kGvThreads = 64 * kGvWaves;
+constexpr int kGvRowsPerWave = 16;
+constexpr int kGvCols = kGvWaves * kGvRowsPerWave;  // weight rows (output columns) per workgroup
+constexpr int kGvInFlight = 4;
+constexpr int kGvMaxRows = 4;
+constexpr int kGvMaxXHalves = 32768;  // rows x D of the fp16 x copy in LDS (64 KB)
+
+template <int CPL>
+__global__ __launch_bounds__(kGvThreads) void grouped_gemv_kernel(GroupedArgs a, int max_rows) {
+  extern __shared__ half8_t xg[];  // [nr][D / 8]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nct = (a.N + kGvCols - 1) / kGvCols;
+  const int g = blockIdx.x / nct, ct = blockIdx.x - g * nct;
+  // Offsets outside [0, R] or decreasing are clamped, as in the tile path.
+  const int r_begin = min(max(a.offsets[g], 0), a.R), r_end = min(max(a.offsets[g + 1], r_begin), a.R);
+  const int nr = min(r_end - r_begin, max_rows);
+  if (nr <= 0) return;  // uniform
+  const int nch = a.D >> 5;
+  const int64_t rowc = a.D / 2, rows = a.D / 16;
+  const float gsa = load_early(a.gsa), gsw = load_early(a.gsw + g);
+
+  for (int i = threadIdx.x; i < nr * nch; i += kGvThreads) {
+    const int t = i / nch, c = i - t * nch;
+    const int64_t r = r_begin + t;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.xc + r * rowc + 16 * c);
+    const uint32_t sb = *reinterpret_cast<const uint16_t*>(a.xs + r * rows + 2 * c);
+    const _Float16 s0 = e4m3_f16(sb & 0xFFu), s1 = e4m3_f16(sb >> 8);
+    half8_t* d = xg + (int64_t)t * (nch * 4) + 4 * c;
+    d[0] = fp4x8_to_f16(v[0], s0);
+    d[1] = fp4x8_to_f16(v[1], s0);
+    d[2] = fp4x8_to_f16(v[2], s1);
+    d[3] = fp4x8_to_f16(v[3], s1);
+  }
+  __syncthreads();
+
+  const float scale = gsa * gsw;
+  const int col_base = ct * kGvCols + wave * kGvRowsPerWave;
+  const uint8_t* wcg = a.wc + (int64_t)g * a.N * rowc;
+  const uint8_t* wsg = a.ws + (int64_t)g * a.N * rows;
+  for (int u0 = 0; u0 < kGvRowsPerWave; u0 += kGvInFlight) {
+    u32x4_t wv[kGvInFlight][CPL];
+    uint32_t wsv[kGvInFlight][CPL];
+#pragma unroll
+    for (int u = 0; u < kGvInFlight; ++u) {
+      const int n = col_base + u0 + u;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        const bool ok = n < a.N && c < nch;
+        const u32x4_t* pc = reinterpret_cast<const u32x4_t*>(wcg + (int64_t)n * rowc + 16 * c);
+        const uint16_t* ps = reinterpret_cast<const uint16_t*>(wsg + (int64_t)n * rows + 2 * c);
+        wv[u][i] = ok ? __builtin_nontemporal_load(pc) : u32x4_t{0u, 0u, 0u, 0u};
+        wsv[u][i] = ok ? __builtin_nontemporal_load(ps) : 0u;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGvInFlight; ++u) {
+      const int n = col_base + u0 + u;
+      float acc[kGvMaxRows];
+#pragma unroll
+      for (int t = 0; t < kGvMaxRows; ++t) acc[t] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = min(lane + 64 * i, nch - 1);  // chunks past D hold zero weights
+        const _Float16 s0 = e4m3_f16(wsv[u][i] & 0xFFu), s1 = e4m3_f16(wsv[u][i] >> 8);
+        const half8_t w0 = fp4x8_to_f16(wv[u][i][0], s0), w1 = fp4x8_to_f16(wv[u][i][1], s0);
+        const half8_t w2 = fp4x8_to_f16(wv[u][i][2], s1), w3 = fp4x8_to_f16(wv[u][i][3], s1);
+#pragma unroll
+        for (int t = 0; t < kGvMaxRows; ++t) {
+          if (t < nr) {
+            const half8_t* xp = xg + (int64_t)t * (nch * 4) + 4 * c;
+            acc[t] += dot8(xp[1], w1, dot8(xp[0], w0, 0.0f));
+            acc[t] += dot8(xp[3], w3, dot8(xp[2], w2, 0.0f));
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kGvMaxRows; ++t) {
+        if (t < nr) {
+          const float y = wave_sum(acc[t]) * scale;
+          if (lane == 0 && n < a.N) a.out[(int64_t)(r_begin + t) * a.N + n] = y;
+        }
+      }
+    }
+  }
+}
+
 __global__ void grouped_offsets_kernel(const int32_t* __restrict__ range, int n, int32_t padded_rows,
                                        int32_t* __restrict__ offsets) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
@@ -127,6 +226,31 @@ static GroupedPlan plan_grouped(int64_t G, int64_t max_rows, int64_t N) {
   for (int ntw = 3; ntw > 1; --ntw)
     if (rtiles * ((N + 128 * ntw - 1) / (128 * ntw)) >= 256) return {128, ntw};
   return {128, 1};
+}
+
+static bool gemv_fits(int64_t max_rows, int64_t D) {
+  return max_rows <= kGvMaxRows && max_rows * D <= kGvMaxXHalves && D <= 16384;
+}
+
+template <int CPL>
+static hipError_t launch_gemv_t(const GroupedArgs& a, int max_rows, int nwg, hipStream_t stream) {
+  const size_t lds = (size_t)max_rows * (size_t)a.D * sizeof(_Float16);
+  grouped_gemv_kernel<CPL><<<nwg, kGvThreads, lds, stream>>>(a, max_rows);
+  return hipGetLastError();
+}
+
+static hipError_t launch_gemv(const GroupedArgs& a, int max_rows, int nwg, hipStream_t stream) {
+  const int cpl = ((a.D >> 5) + 63) / 64;  // 32-element chunks per lane, D <= 16384
+  switch (cpl) {
+    case 1: return launch_gemv_t<1>(a, max_rows, nwg, stream);
+    case 2: return launch_gemv_t<2>(a, max_rows, nwg, stream);
+    case 3: return launch_gemv_t<3>(a, max_rows, nwg, stream);
+    case 4: return launch_gemv_t<4>(a, max_rows, nwg, stream);
+    case 5: return launch_gemv_t<5>(a, max_rows, nwg, stream);
+    case 6: return launch_gemv_t<6>(a, max_rows, nwg, stream);
+    case 7: return launch_gemv_t<7>(a, max_rows, nwg, stream);
+    default: return launch_gemv_t<8>(a, max_rows, nwg, stream);
+  }
 }
 
 }  // namespace nvr
@@ -180,6 +304,12 @@ int grouped_gemm(const uint8_t* x_codes, const uint8_t* x_scales, const float* g
                      0, 0, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (nvr::gemv_fits(max_rows, D)) {
+    const int64_t nwg = G * ((N + nvr::kGvCols - 1) / nvr::kGvCols);
+    if (nwg >= (int64_t(1) << 31)) return ROUTER_EUNSUPPORTED;
+    e = nvr::launch_gemv(a, (int)max_rows, (int)nwg, s);
+    return e == hipSuccess ? ROUTER_OK : ROUTER_EHIP;
+  }
   switch (p.bm * 8 + p.ntw) {
     case 32 * 8 + 1: e = launch_grouped<32, 1>(a, max_rows, s); break;
     case 64 * 8 + 1: e = launch_grouped<64, 1>(a, max_rows, s); break;

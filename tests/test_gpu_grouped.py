@@ -106,7 +106,11 @@ def synth(shape, seed, scale=1.0):
     (2, 100, 1024, 256),   # 128-row tiles, ragged rows
     (3, 200, 2048, 520),   # 128-row tiles, wider column tiles, ragged columns
     (1, 64, 256, 128),     # one group, exactly one tile
-    (5, 2, 1056, 40),      # D not a multiple of 128
+    (5, 2, 1056, 40),      # D not a multiple of 128 (decode-size groups: the GEMV path)
+    (3, 4, 2048, 200),     # GEMV path: four rows per group, columns past a 64-column tile
+    (2, 2, 16384, 70),     # GEMV path: largest D it takes, eight chunks per lane
+    (4, 1, 4128, 64),      # GEMV path: the last chunk of each lane's row ragged
+    (2, 5, 512, 96),       # five rows per group: the MFMA path again
 ])
 def test_grouped_shapes(dev, ws, G, P, D, N):
     log(f"grouped G={G} P={P} D={D} N={N}")
@@ -137,6 +141,24 @@ def test_general_offsets_with_an_empty_group(dev, ws):
     ref = grouped_ref(x, offsets, w)
     assert_outputs(Y[:40], ref["Y"][:40], ref["A"][:40], "general offsets")
     assert np.all(Y[40:] == -123.0)
+
+
+def test_gemv_general_offsets_and_row_bound(dev, ws):
+    """The decode-size (GEMV) path with offsets that are not a multiple of one size, an empty group, rows of no
+    group, and a max_rows bound below a group's size: uncomputed rows keep the output's fill."""
+    offsets = [0, 2, 2, 5]
+    G, R, D, N = 3, 7, 1024, 130
+    x = synth((R, D), 91)
+    w = synth((G, N, D), 92, 0.02)
+    log("GEMV path: offsets [0, 2, 2, 5], 7 rows, max_rows 3 then 2")
+    _, _, Y = run_grouped(dev, ws, x, w, offsets, 3, fill=-5.0)
+    ref = grouped_ref(x, offsets, w)
+    assert_outputs(Y[:5], ref["Y"][:5], ref["A"][:5], "GEMV general offsets")
+    assert np.all(Y[5:] == -5.0)
+    _, _, Y2 = run_grouped(dev, ws, x, w, offsets, 2, fill=-5.0)
+    assert_outputs(Y2[:4], ref["Y"][:4], ref["A"][:4], "GEMV, max_rows 2")
+    assert np.all(Y2[4:] == -5.0)
+    assert np.array_equal(Y2[:4], Y[:4])  # the same rows, the same bits
 
 
 def test_bound_on_rows_per_group(dev, ws):
@@ -192,25 +214,33 @@ def test_full_size_prefill(dev, ws):
     full_size_case(dev, ws, 13, np.unique(np.concatenate([edges, extra])))
 
 
-def test_graph_capture_replays_match_eager(dev, ws):
-    """Offsets, the flattened quantize and the grouped GEMM captured in one graph and replayed."""
-    c = wl.GROUPED_CONFIGS[11]
-    x = to_dev(wl.make_grouped_x(11), dev)
-    wg = rt.quantize_grouped_weights(to_dev(np.stack([wl.make_grouped_w(11, g) for g in range(c.G)]), dev), ws)
-    rng_buf = torch.arange(c.G + 1, dtype=torch.int32, device=dev)
-    off = torch.empty(c.G + 1, dtype=torch.int32, device=dev)
-    xq = rt.empty_nvfp4(c.G * c.P, c.D, dev)
-    out = torch.empty((c.G * c.P, c.N), dtype=torch.float32, device=dev)
+@pytest.mark.parametrize("shape", ["tiles", "gemv"])
+def test_graph_capture_replays_match_eager(dev, ws, shape):
+    """Offsets, the flattened quantize and the grouped GEMM captured in one graph and replayed (the MFMA tile
+    path at 5 rows per group, the GEMV path at 2)."""
+    if shape == "tiles":
+        c = wl.GROUPED_CONFIGS[11]
+        G, P, D, N = c.G, c.P, c.D, c.N
+        xb, wb = wl.make_grouped_x(11), np.stack([wl.make_grouped_w(11, g) for g in range(c.G)])
+    else:
+        G, P, D, N = 3, 2, 512, 100
+        xb, wb = synth((G * P, D), 31), synth((G, N, D), 32, 0.02)
+    x = to_dev(xb, dev)
+    wg = rt.quantize_grouped_weights(to_dev(wb, dev), ws)
+    rng_buf = torch.arange(G + 1, dtype=torch.int32, device=dev)
+    off = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    xq = rt.empty_nvfp4(G * P, D, dev)
+    out = torch.empty((G * P, N), dtype=torch.float32, device=dev)
 
     def step():
-        rt.grouped_offsets(rng_buf, c.P, out=off)
+        rt.grouped_offsets(rng_buf, P, out=off)
         rt.quantize(x, ws, out=xq)
-        rt.grouped_gemm(xq, wg, off, c.P, out=out)
+        rt.grouped_gemm(xq, wg, off, P, out=out)
 
     step()
     torch.cuda.synchronize()
     eager = out.clone()
-    log("graph capture of the grouped layer")
+    log(f"graph capture of the grouped layer ({shape})")
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
