@@ -492,6 +492,24 @@ def test_forward_matches_oracle(dev, ws, cfg, T, D, E, k, want_logits):
 
 
 @pytest.mark.parametrize("cfg", [2, 3])
+def test_forward_is_deterministic(dev, ws, cfg):
+    """router_forward twice on the same inputs (one launch at T = 1, two at T = 64): identical bits."""
+    c = wl.CONFIGS[cfg]
+    x, w, bias = wl.make_x(cfg), wl.make_w(cfg), wl.make_bias(cfg)
+    log(f"forward determinism cfg {cfg}")
+    wq = gpu_quant(w, dev, ws)
+    xd, b = to_dev(x, dev), torch.from_numpy(bias).to(dev)
+    runs = []
+    for _ in range(2):
+        xq, (idx, wts, logits) = rt.forward(xd, wq, b, c.k, c.routed_scale, ws, want_logits=True)
+        torch.cuda.synchronize()
+        runs.append((xq.codes.cpu().numpy(), idx.cpu().numpy(), wts.cpu().numpy().view(np.uint32),
+                     logits.cpu().numpy().view(np.uint32)))
+    for a, b2 in zip(*runs):
+        assert np.array_equal(a, b2)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
 def test_forward_static_scale_override(dev, ws, cfg):
     c = wl.CONFIGS[cfg]
     x, w, bias = wl.make_x(cfg, 3), wl.make_w(cfg, 3), wl.make_bias(cfg, 3)
