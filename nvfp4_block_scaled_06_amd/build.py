@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4_router.so")
-SOURCES = ["router_api.hip", "quantize.hip", "gate.hip", "gate_decode.hip", "gate_batch.hip", "probe.hip", "lmhead.hip", "grouped.hip"]
+SOURCES = ["router_api.hip", "quantize.hip", "gate.hip", "gate_mfma_e4.hip", "gate_mfma_e8.hip", "gate_mfma_e16.hip", "gate_mfma_e24.hip", "gate_mfma_e32.hip", "gate_decode.hip", "gate_batch.hip", "probe.hip", "lmhead.hip", "grouped.hip"]
 
 COMPILE_FLAGS = [
     "--offload-arch=gfx950",

@@ -43,7 +43,7 @@ struct GroupedArgs {
   int nwg;
 };
 
-template <int BM, int NTW, int KS>
+template <int BM, int NTW, int KS, bool STAGED>
 __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_eu(KS, KS))) void grouped_mfma_kernel(
     GroupedArgs a) {
   static_assert(KS == mma_ksplit<BM, NTW>(), "K groups as the main loop has them");
@@ -51,6 +51,7 @@ __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_e
   static_assert(KS == 1 || BM * BN * sizeof(float) <= sizeof(_Float16) * KS * 2 * BM * kMmaARow,
                 "the epilogue's partial sums fit in the A tiles' LDS");
   __shared__ __attribute__((aligned(16))) _Float16 abuf[KS][2][BM * kMmaARow];
+  __shared__ __attribute__((aligned(16))) uint8_t swin[STAGED ? mma_win_bytes<BM, NTW>() : 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wt = wave & 3, grp = wave >> 2;
   // Workgroup ids go to the 8 XCDs in turn; consecutive tiles (the column
   // tiles of one row tile first) are numbered onto one XCD, so a row tile's
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_e
                                                  a.ws + wrow0 * rows, nc, a.D, wt, lane);
   constexpr int NS = mma_sets<BM, NTW>();
   f32x16_t acc[NS][BM / 32][NTW];
-  mma_mainloop<BM, NTW, KS>(P, a.D, a.nsteps, &abuf[0][0][0], lane, acc);
+  mma_mainloop<BM, NTW, KS, STAGED>(P, a.D, a.nsteps, &abuf[0][0][0], swin, lane, acc);
 
   // 32x32 accumulator layout: value v of lane (r, h) is row 8(v/4) + 4h +
   // v%4, column r of its tile; wavefront wt holds the column tiles wt + 4t.
@@ -266,7 +267,10 @@ hipError_t launch_grouped(nvr::GroupedArgs a, int64_t max_rows, hipStream_t stre
   a.nsteps = nvr::mma_padded_steps<BM, NTW>(a.D);
   a.nwg = a.G * a.row_tiles * a.col_tiles;
   constexpr int KS = nvr::mma_ksplit<BM, NTW>();
-  nvr::grouped_mfma_kernel<BM, NTW, KS><<<a.nwg, nvr::kMmaThreads * KS, 0, stream>>>(a);
+  // Scale windows take 16-byte loads: rows of D / 16 scale bytes must keep
+  // them aligned.
+  if (a.D % 256 == 0) nvr::grouped_mfma_kernel<BM, NTW, KS, true><<<a.nwg, nvr::kMmaThreads * KS, 0, stream>>>(a);
+  else nvr::grouped_mfma_kernel<BM, NTW, KS, false><<<a.nwg, nvr::kMmaThreads * KS, 0, stream>>>(a);
   return hipGetLastError();
 }
 

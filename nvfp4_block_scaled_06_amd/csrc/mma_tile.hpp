@@ -20,6 +20,15 @@
 //  * Loads are raw buffer loads whose descriptors cover only the tile's
 //    rows, so rows past the end and chunks past D read zeros without a
 //    branch; they run mma_ring() steps ahead in a register ring.
+//  * Scales (STAGED, D a multiple of 256): the E4M3 bytes of kMmaWin
+//    consecutive K steps of every A and B row of the tile are loaded ahead
+//    by the whole workgroup, 16 bytes per lane and four lanes per row, into
+//    one of two LDS windows; each step reads its scale bytes there. A vector
+//    load costs the address unit about one pass per cache line it touches,
+//    whatever its width, so a per-step load of two scale bytes per lane
+//    cost as much as a 16-byte code load (measured on gfx950: ~56 cycles per
+//    compute unit for 16 rows, for 2 bytes or 16 per lane). Otherwise each
+//    step loads its scale bytes with its codes.
 #pragma once
 
 #include "gate_common.hpp"
@@ -36,6 +45,30 @@ constexpr int mma_ring() {
 }
 constexpr int kMmaARow = 136;  // LDS row stride of the A tile in halves (128 values + 8 pad)
 
+
+// Eight E2M1 codes times the block scale s, as fp16 (exact), like
+// fp4x8_to_f16 but with its instructions in a fixed order: the four converts
+// are all issued before the first multiply: left to itself the compiler
+// alternates them through one temporary register, a chain in which every
+// instruction waits for the one before it (one wavefront per SIMD has no
+// other wavefront to fill those cycles).
+__device__ __forceinline__ half8_t fp4x8_scaled(uint32_t c, _Float16 s) {
+  const half2_t ss = {s, s};
+  half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0);
+  half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1);
+  half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2);
+  half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3);
+  asm volatile("" : "+v"(h0), "+v"(h1), "+v"(h2), "+v"(h3));
+  h0 *= ss;
+  h1 *= ss;
+  h2 *= ss;
+  h3 *= ss;
+  return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+__device__ __forceinline__ half8_t fp4x8_scaled(uint32_t c, half2_t s2, int sel) {
+  return fp4x8_scaled(c, sel ? s2[1] : s2[0]);
+}
 
 // Token rows per thread in the A tile (4 threads per row): one slot per 64
 // rows; with BM = 32 only threads 0..127 have a row.
@@ -105,7 +138,7 @@ __device__ __forceinline__ MmaPtrs<BM, NTW> mma_ptrs(const uint8_t* xc, const ui
   return P;
 }
 
-template <int BM, int NTW>
+template <bool STAGED, int BM, int NTW>
 __device__ __forceinline__ void mma_load(MmaRegs<BM, NTW>& R, const MmaPtrs<BM, NTW>& P, int D, int step) {
   const int k0 = step * 128;
   const bool aok = k0 + P.ka < D;
@@ -113,7 +146,7 @@ __device__ __forceinline__ void mma_load(MmaRegs<BM, NTW>& R, const MmaPtrs<BM, 
   for (int i = 0; i < mma_row_slots<BM>(); ++i) {
     const uint32_t oc = aok ? P.a[i] + 64 * step : kMmaOob, os = aok ? P.as[i] + 8 * step : kMmaOob;
     R.a[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(P.xc, oc, 0, 0));
-    R.as[i] = __builtin_amdgcn_raw_buffer_load_b16(P.xs, os, 0, 0);
+    if constexpr (!STAGED) R.as[i] = __builtin_amdgcn_raw_buffer_load_b16(P.xs, os, 0, 0);
   }
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -123,25 +156,72 @@ __device__ __forceinline__ void mma_load(MmaRegs<BM, NTW>& R, const MmaPtrs<BM, 
       const uint32_t oc = bok ? P.b[t] + 64 * step + 32 * c : kMmaOob;
       const uint32_t os = bok ? P.bs[t] + 8 * step + 4 * c : kMmaOob;
       R.b[t][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(P.wc, oc, 0, 0));
-      R.bs[t][c] = __builtin_amdgcn_raw_buffer_load_b16(P.ws, os, 0, 0);
+      if constexpr (!STAGED) R.bs[t][c] = __builtin_amdgcn_raw_buffer_load_b16(P.ws, os, 0, 0);
     }
   }
 }
 
+// Scale windows. LDS layout per window: row (A rows 0 .. BM - 1, then the
+// 128 NTW B rows) at kMmaWinLd bytes, its kMmaWin steps' 8 scale bytes each
+// in step order. The row stride of 17 dwords makes the reads of 32 rows at
+// one offset conflict-free.
+constexpr int kMmaWin = 8;     // K steps per scale window
+constexpr int kMmaWinLd = 68;  // LDS bytes per row and window (64 + 4)
+
+template <int BM, int NTW>
+constexpr int mma_win_bytes() { return 2 * (BM + 128 * NTW) * kMmaWinLd; }  // both windows
+
+// One window's loads, in flight between their issue and their LDS store:
+// piece p = tid + NT j (j < NL) is bytes [16 (p % 4), +16) of the window's
+// 64 bytes of row p / 4. A wavefront's 64 pieces are 16 whole rows, all of
+// A or all of B. Pieces past the row's D / 16 scale bytes (the last window)
+// and rows past the tile's valid rows load zeros.
+template <int BM, int NTW, int KS>
+struct ScaleWin {
+  static constexpr int ROWS = BM + 128 * NTW, NP = 4 * ROWS, NT = kMmaThreads * KS, NL = (NP + NT - 1) / NT;
+  u32x4_t v[NL];
+
+  template <int J>
+  __device__ __forceinline__ void load(const MmaPtrs<BM, NTW>& P, int win, int rows) {
+    const int tid = threadIdx.x;
+    const int p = tid + NT * J, row = p >> 2, part = p & 3;
+    // The wavefront's first row, as a scalar: A or B is uniform per wavefront.
+    const int row_w = __builtin_amdgcn_readfirstlane((tid & ~63) + NT * J) >> 2;
+    const bool isA = row_w < BM;
+    const int rr = isA ? row : row - BM;
+    const int byte = 64 * win + 16 * part;
+    const uint32_t off = (p < NP && byte < rows) ? (uint32_t)(rr * rows + byte) : kMmaOob;
+    v[J] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(isA ? P.xs : P.ws, off, 0, 0));
+  }
+
+  template <int J>
+  __device__ __forceinline__ void store(uint8_t* buf) const {
+    const int p = threadIdx.x + NT * J;
+    if (NP % NT == 0 || p < NP) {
+      uint32_t* d = reinterpret_cast<uint32_t*>(buf + (p >> 2) * kMmaWinLd + 16 * (p & 3));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = v[J][i];
+    }
+  }
+};
+
+__device__ __forceinline__ uint32_t lds_u16(const uint8_t* p) { return *reinterpret_cast<const uint16_t*>(p); }
+
 // This thread's A chunks, converted, into the LDS tile.
 template <int BM, int NTW>
-__device__ __forceinline__ void mma_store_a(const MmaRegs<BM, NTW>& R, _Float16* abuf) {
+__device__ __forceinline__ void mma_store_a(const MmaRegs<BM, NTW>& R, const uint32_t (&asw)[mma_row_slots<BM>()],
+                                            _Float16* abuf) {
   const int tid = threadIdx.x & (kMmaThreads - 1), q = tid & 3;
 #pragma unroll
   for (int i = 0; i < mma_row_slots<BM>(); ++i) {
     const int r = (tid >> 2) + 64 * i;
     if (r >= BM) break;  // BM = 32: threads 128..255 hold no row
-    const _Float16 s0 = e4m3_f16(R.as[i] & 0xFFu), s1 = e4m3_f16(R.as[i] >> 8);
+    const _Float16 s0 = e4m3_f16(asw[i] & 0xFFu), s1 = e4m3_f16(asw[i] >> 8);
     half8_t* dst = reinterpret_cast<half8_t*>(abuf + r * kMmaARow + 32 * q);
-    dst[0] = fp4x8_to_f16(R.a[i][0], s0);
-    dst[1] = fp4x8_to_f16(R.a[i][1], s0);
-    dst[2] = fp4x8_to_f16(R.a[i][2], s1);
-    dst[3] = fp4x8_to_f16(R.a[i][3], s1);
+    dst[0] = fp4x8_scaled(R.a[i][0], s0);
+    dst[1] = fp4x8_scaled(R.a[i][1], s0);
+    dst[2] = fp4x8_scaled(R.a[i][2], s1);
+    dst[3] = fp4x8_scaled(R.a[i][3], s1);
   }
 }
 
@@ -171,8 +251,9 @@ constexpr int mma_ksplit() {
 // experts; with two groups the fences win). The A fragments of row tile
 // rt + 1 are read right after their last use in row tile rt.
 template <int BM, int NTW>
-__device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& Rc, const _Float16* abuf, const MmaRegs<BM, NTW>& Rn,
-                                         _Float16* abuf_n, int lane,
+__device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& Rc, const uint32_t (&bsw)[NTW][2],
+                                         const _Float16* abuf, const MmaRegs<BM, NTW>& Rn,
+                                         const uint32_t (&asw)[mma_row_slots<BM>()], _Float16* abuf_n, int lane,
                                          f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
   constexpr int NS = mma_sets<BM, NTW>();
   constexpr int SL = mma_row_slots<BM>();
@@ -186,26 +267,26 @@ __device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& Rc, const _Floa
   for (int t = 0; t < NTW; ++t)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      bsc[t][c][0] = e4m3_f16(Rc.bs[t][c] & 0xFFu);
-      bsc[t][c][1] = e4m3_f16(Rc.bs[t][c] >> 8);
+      bsc[t][c][0] = e4m3_f16(bsw[t][c] & 0xFFu);
+      bsc[t][c][1] = e4m3_f16(bsw[t][c] >> 8);
     }
 #pragma unroll
   for (int i = 0; i < SL; ++i) {
-    asc[i][0] = e4m3_f16(Rn.as[i] & 0xFFu);
-    asc[i][1] = e4m3_f16(Rn.as[i] >> 8);
+    asc[i][0] = e4m3_f16(asw[i] & 0xFFu);
+    asc[i][1] = e4m3_f16(asw[i] >> 8);
   }
   half8_t B[NTW][8];
   // B unit m feeds MFMA m of the first row tile: K slice j = m / NTW of
   // expert tile t = m % NTW.
   auto bunit = [&](auto uc) {
     constexpr int m = decltype(uc)::value, j = m / NTW, t = m % NTW;
-    B[t][j] = fp4x8_to_f16(Rc.b[t][j / 4][j % 4], bsc[t][j / 4][(j % 4) >> 1]);
+    B[t][j] = fp4x8_scaled(Rc.b[t][j / 4][j % 4], bsc[t][j / 4][(j % 4) >> 1]);
   };
   auto aunit = [&](auto uc) {
     constexpr int i = decltype(uc)::value / 4, q = decltype(uc)::value % 4;
     const int row = (tid >> 2) + 64 * i;
     if (BM >= 64 || row < BM)  // BM = 32: threads 128..255 hold no row
-      reinterpret_cast<half8_t*>(abuf_n + row * kMmaARow + 32 * q4)[q] = fp4x8_to_f16(Rn.a[i][q], asc[i][q >> 1]);
+      reinterpret_cast<half8_t*>(abuf_n + row * kMmaARow + 32 * q4)[q] = fp4x8_scaled(Rn.a[i][q], asc[i][q >> 1]);
   };
   const _Float16* arow = abuf + r * kMmaARow + 32 * h;
   auto afrag = [&](int rt, int j) {
@@ -231,16 +312,44 @@ __device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& Rc, const _Floa
 // The K loop of one workgroup tile: KS K groups of four wavefronts (group
 // grp takes K steps grp, grp + KS, ...), loads RING steps ahead in a register
 // ring, A converted into the group's two LDS tiles (abuf + (2 grp + i) BM
-// kMmaARow halves), B converted in registers. nsteps is padded to a multiple
-// of KS times the ring depth; padding steps load nothing (k >= D) and add
-// zeros. Leaves acc[0] holding this group's sums (the two accumulator sets
+// kMmaARow halves), B converted in registers. One iteration covers a scale
+// window of kMmaWin steps (kMmaWin / (KS RING) ring passes); nsteps is
+// padded to a multiple of it, and padding steps load nothing (k >= D) and
+// add zeros. STAGED: the next window's scale loads are spread over the
+// first half of the window's positions (a position is one step of each
+// group, ending at a barrier) and their LDS stores over the next ones, all
+// before the barrier ahead of the last position, whose A conversion (for
+// the next window's first steps) reads them. swin holds mma_win_bytes()
+// bytes. Leaves acc[0] holding this group's sums (the two accumulator sets
 // added).
-template <int BM, int NTW, int KS>
+template <int BM, int NTW, int KS, bool STAGED>
 __device__ __forceinline__ void mma_mainloop(const MmaPtrs<BM, NTW>& P, int D, int nsteps, _Float16* abuf_base,
-                                             int lane, f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
-  constexpr int NS = mma_sets<BM, NTW>();
+                                             uint8_t* swin, int lane,
+                                             f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
+  constexpr int NS = mma_sets<BM, NTW>(), SL = mma_row_slots<BM>();
+  constexpr int RING = mma_ring<BM, NTW>(), SPI = KS * RING, IPW = kMmaWin / SPI, POS = IPW * RING;
+  static_assert(kMmaWin % SPI == 0, "a window holds whole ring passes");
   const int grp = (threadIdx.x >> 6) >> 2;
+  const int tid = threadIdx.x & (kMmaThreads - 1), q4 = tid & 3, r = lane & 31, h = lane >> 5;
+  const int rows = D / 16;
   auto abuf = [&](int i) { return abuf_base + (2 * grp + i) * (BM * kMmaARow); };
+  constexpr int WB = (BM + 128 * NTW) * kMmaWinLd;  // one window
+  // This lane's scale words of step-in-window sw from window buffer wb:
+  // its A rows (the A conversion's 2 bytes at 2 q4) and its B rows (2 bytes
+  // per 64-element chunk c at 4c + 2h).
+  auto a_words = [&](int wb, int sw, uint32_t (&w)[SL]) {
+#pragma unroll
+    for (int i = 0; i < SL; ++i)
+      w[i] = lds_u16(swin + wb * WB + min((tid >> 2) + 64 * i, BM - 1) * kMmaWinLd + 8 * sw + 2 * q4);
+  };
+  auto b_words = [&](int wb, int sw, uint32_t (&w)[NTW][2]) {
+    const int wt = (threadIdx.x >> 6) & 3;
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        w[t][c] = lds_u16(swin + wb * WB + (BM + (wt + 4 * t) * 32 + r) * kMmaWinLd + 8 * sw + 4 * c + 2 * h);
+  };
 #pragma unroll
   for (int q = 0; q < NS; ++q)
 #pragma unroll
@@ -249,25 +358,61 @@ __device__ __forceinline__ void mma_mainloop(const MmaPtrs<BM, NTW>& P, int D, i
       for (int t = 0; t < NTW; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[q][rt][t][v] = 0.0f;
-  constexpr int RING = mma_ring<BM, NTW>();
   MmaRegs<BM, NTW> R[RING];
 #pragma unroll
-  for (int p = 0; p < RING; ++p) mma_load<BM, NTW>(R[p], P, D, KS * p + grp);
-  mma_store_a<BM, NTW>(R[0], abuf(0));
-  __syncthreads();
-  for (int s0 = 0; s0 < nsteps; s0 += KS * RING) {
-    // The A tiles alternate with this group's step count, RING it + p: with
-    // an odd ring the parity of p alone does not alternate across passes.
-    const int par = (RING & 1) ? (s0 / (KS * RING)) & 1 : 0;
+  for (int p = 0; p < RING; ++p) mma_load<STAGED, BM, NTW>(R[p], P, D, KS * p + grp);
+  ScaleWin<BM, NTW, KS> win;
+  uint32_t aw[SL];
+  if constexpr (STAGED) {
+    static_for<0, ScaleWin<BM, NTW, KS>::NL>([&](auto jc) { win.template load<decltype(jc)::value>(P, 0, rows); });
+    static_for<0, ScaleWin<BM, NTW, KS>::NL>([&](auto jc) { win.template store<decltype(jc)::value>(swin); });
+    __syncthreads();
+    a_words(0, grp, aw);
+  } else {
 #pragma unroll
-    for (int p = 0; p < RING; ++p) {
-      // Step s0 + KS p + grp: A from tile (p + par) & 1, B from R[p]; the
-      // next step's A (R[(p + 1) % RING]) into the other tile; then R[p]
-      // (fully used) reloads the step RING ahead.
-      mma_step<BM, NTW>(R[p], abuf((p + par) & 1), R[(p + 1) % RING], abuf((p + 1 + par) & 1), lane, acc);
-      mma_load<BM, NTW>(R[p], P, D, s0 + KS * (p + RING) + grp);
-      __syncthreads();
-    }
+    for (int i = 0; i < SL; ++i) aw[i] = R[0].as[i];
+  }
+  mma_store_a<BM, NTW>(R[0], aw, abuf(0));
+  __syncthreads();
+  for (int s0 = 0; s0 < nsteps; s0 += kMmaWin) {
+    const int wi = s0 / kMmaWin, wb = wi & 1;
+    static_for<0, IPW>([&](auto ic) {
+      constexpr int it = decltype(ic)::value;
+      static_for<0, RING>([&](auto pc) {
+        constexpr int p = decltype(pc)::value, pos = it * RING + p;
+        // Step s0 + it SPI + KS p + grp: A from tile pos & 1, B from R[p];
+        // the group's next step's A (R[(p + 1) % RING]) into the other
+        // tile; then R[p] (fully used) reloads the step RING ahead.
+        constexpr int sw = it * SPI + KS * p;  // step in window, less grp
+        uint32_t bw[NTW][2], an[SL];
+        if constexpr (STAGED) {
+          constexpr int NL = ScaleWin<BM, NTW, KS>::NL, NLP = POS / 2;
+          if constexpr (pos < NLP)
+            static_for<pos * NL / NLP, (pos + 1) * NL / NLP>(
+                [&](auto jc) { win.template load<decltype(jc)::value>(P, wi + 1, rows); });
+          b_words(wb, sw + grp, bw);
+          // The next step is the next window's when sw + KS reaches kMmaWin.
+          if constexpr (sw + KS < kMmaWin) a_words(wb, sw + KS + grp, an);
+          else a_words(wb ^ 1, sw + KS - kMmaWin + grp, an);
+        } else {
+#pragma unroll
+          for (int t = 0; t < NTW; ++t)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) bw[t][c] = R[p].bs[t][c];
+#pragma unroll
+          for (int i = 0; i < SL; ++i) an[i] = R[(p + 1) % RING].as[i];
+        }
+        mma_step<BM, NTW>(R[p], bw, abuf(pos & 1), R[(p + 1) % RING], an, abuf((pos + 1) & 1), lane, acc);
+        mma_load<STAGED, BM, NTW>(R[p], P, D, s0 + it * SPI + KS * (p + RING) + grp);
+        if constexpr (STAGED) {
+          constexpr int NL = ScaleWin<BM, NTW, KS>::NL, NSP = POS - 1 - POS / 2;
+          if constexpr (pos >= POS / 2 && pos < POS - 1)
+            static_for<(pos - POS / 2) * NL / NSP, (pos - POS / 2 + 1) * NL / NSP>(
+                [&](auto jc) { win.template store<decltype(jc)::value>(swin + (wb ^ 1) * WB); });
+        }
+        __syncthreads();
+      });
+    });
   }
   if (NS == 2) {
 #pragma unroll
@@ -277,12 +422,12 @@ __device__ __forceinline__ void mma_mainloop(const MmaPtrs<BM, NTW>& P, int D, i
   }
 }
 
-// K steps of 128 elements for D, padded to a multiple of KS times the ring depth.
+// K steps of 128 elements for D, padded to a whole number of scale windows
+// (each a whole number of K groups times the ring depth).
 template <int BM, int NTW>
 inline int mma_padded_steps(int64_t D) {
-  constexpr int G = mma_ksplit<BM, NTW>() * mma_ring<BM, NTW>();
   const int steps = (int)((D + 127) / 128);
-  return (steps + G - 1) / G * G;
+  return (steps + kMmaWin - 1) / kMmaWin * kMmaWin;
 }
 
 }  // namespace nvr
