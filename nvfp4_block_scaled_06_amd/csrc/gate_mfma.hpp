@@ -58,11 +58,12 @@ struct MmaArgs {
 
 // Epilogue rows per pass: 64 when two K groups share the work and the rows
 // fit the LDS, else 32. Each wavefront routes LR / (4 KS) rows per pass, as
-// sets of four.
+// sets of four, two sets per call (interleaved, for latency hiding: with one
+// wavefront per SIMD this was worth ~6 % of the large-prefill gate).
 template <int BM, int J16, int KS>
 constexpr int epi_rows() { return KS == 2 && BM >= 64 && J16 <= 24 ? 64 : 32; }
 template <int BM, int J16, int KS>
-constexpr int epi_sets() { return KS == 2 ? epi_rows<BM, J16, KS>() / 32 : 1; }
+constexpr int epi_sets() { return KS == 2 ? epi_rows<BM, J16, KS>() / 32 : 2; }
 
 // LDS row stride of the epilogue's logits, in floats: the router reads 16 J16
 // entries per row (16 bytes at a time), and the accumulators of a whole
@@ -120,13 +121,16 @@ __device__ __forceinline__ void route_tile(const TileArgs& a, int ncb, int rb, i
     static_for<0, BM / 32>(store_pass);
     if (!arrive_last(&a.counters[rb], ncb, s_last)) return;
   }
-  // Passes of LR tokens; compile-time row tile indexes keep the accumulator
-  // indexes static (a runtime loop over this body would put them in scratch).
+  // Passes of LR tokens, as a runtime loop so that the routing code exists
+  // once: unrolled per pass and per call it made the largest kernels several
+  // times the instruction cache, and their routing ran from misses. Filling
+  // a pass from the accumulators takes compile-time row tile indexes (runtime
+  // ones would put them in scratch), so each pass's fill has its own branch.
   constexpr int LR = epi_rows<BM, J16, KS>(), NSET = epi_sets<BM, J16, KS>();
-  auto pass = [&](auto pc) {
-    constexpr int p = decltype(pc)::value;
+#pragma unroll 1
+  for (int p = 0; p < BM / LR; ++p) {
     const int base = row0 + p * LR;
-    if (base >= a.T) return;  // uniform
+    if (base >= a.T) break;  // uniform
     const int nrows = min(LR, a.T - base);
     __syncthreads();
     if (ncb > 1) {
@@ -149,16 +153,20 @@ __device__ __forceinline__ void route_tile(const TileArgs& a, int ncb, int rb, i
 #pragma unroll
         for (int cc = 0; cc < J16 / 4; ++cc) lg[(wave + 4 * KS * rr) * ldE + lane + 64 * cc] = v[rr][cc];
     } else {
-      static_for<0, LR / 32>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        tile_to_lds(IntC<p * (LR / 32) + i>{}, 32 * i);
+      static_for<0, BM / LR>([&](auto pc) {
+        constexpr int pp = decltype(pc)::value;
+        if (p == pp)
+          static_for<0, LR / 32>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            tile_to_lds(IntC<pp * (LR / 32) + i>{}, 32 * i);
+          });
       });
     }
     __syncthreads();
     // Wavefront w routes rows RW w .. RW w + RW - 1 (RW = LR / 4KS), in calls
     // of NSET interleaved sets of four.
     constexpr int RW = LR / (4 * KS);
-#pragma unroll
+#pragma unroll 1
     for (int c0 = 0; c0 < RW / 4; c0 += NSET) {
       const float* Lr[NSET];
       bool vr[NSET];
@@ -181,8 +189,7 @@ __device__ __forceinline__ void route_tile(const TileArgs& a, int ncb, int rb, i
         a.logits_out[(int64_t)(base + mm) * E + e] = lg[mm * ldE + e];
       }
     }
-  };
-  static_for<0, BM / LR>(pass);
+  }
   if (ncb > 1) release_counter(&a.counters[rb]);
 }
 
