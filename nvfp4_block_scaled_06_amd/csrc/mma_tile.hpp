@@ -66,6 +66,13 @@ __device__ __forceinline__ half8_t fp4x8_scaled(uint32_t c, _Float16 s) {
   return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
+// The two E4M3 scale bytes in the low half of w as f16 values (exact: every
+// E4M3 value is an f16 value; the bytes 0x7F and 0xFF decode to NaN, as the
+// format defines them).
+__device__ __forceinline__ half2_t e4m3x2_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+}
+
 __device__ __forceinline__ half8_t fp4x8_scaled(uint32_t c, half2_t s2, int sel) {
   return fp4x8_scaled(c, sel ? s2[1] : s2[0]);
 }
@@ -140,6 +147,22 @@ __device__ __forceinline__ MmaPtrs<BM, NTW> mma_ptrs(const uint8_t* xc, const ui
 
 template <bool STAGED, int BM, int NTW>
 __device__ __forceinline__ void mma_load(MmaRegs<BM, NTW>& R, const MmaPtrs<BM, NTW>& P, int D, int step) {
+  if constexpr (STAGED) {
+    // D is a multiple of 256, so every step but the padding ones lies
+    // wholly before D. Those read the last real step again, through the
+    // scalar offset (the loop computes no addresses); their scales in the
+    // window are zero, so they add nothing (E2M1 codes are always finite).
+    const int so = 64 * min(step, D / 128 - 1);
+#pragma unroll
+    for (int i = 0; i < mma_row_slots<BM>(); ++i)
+      R.a[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(P.xc, P.a[i], so, 0));
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+        R.b[t][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(P.wc, P.b[t] + 32 * c, so, 0));
+    return;
+  }
   const int k0 = step * 128;
   const bool aok = k0 + P.ka < D;
 #pragma unroll
@@ -216,7 +239,8 @@ __device__ __forceinline__ void mma_store_a(const MmaRegs<BM, NTW>& R, const uin
   for (int i = 0; i < mma_row_slots<BM>(); ++i) {
     const int r = (tid >> 2) + 64 * i;
     if (r >= BM) break;  // BM = 32: threads 128..255 hold no row
-    const _Float16 s0 = e4m3_f16(asw[i] & 0xFFu), s1 = e4m3_f16(asw[i] >> 8);
+    const half2_t sp = e4m3x2_f16(asw[i]);
+    const _Float16 s0 = sp[0], s1 = sp[1];
     half8_t* dst = reinterpret_cast<half8_t*>(abuf + r * kMmaARow + 32 * q);
     dst[0] = fp4x8_scaled(R.a[i][0], s0);
     dst[1] = fp4x8_scaled(R.a[i][1], s0);
@@ -262,31 +286,25 @@ __device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& Rc, const uint3
   constexpr int NA = 4 * SL;               // A units
   const int r = lane & 31, h = lane >> 5;
   const int tid = threadIdx.x & (kMmaThreads - 1), q4 = tid & 3;
-  _Float16 bsc[NTW][2][2], asc[SL][2];
+  half2_t bsc[NTW][2], asc[SL];
 #pragma unroll
   for (int t = 0; t < NTW; ++t)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bsc[t][c][0] = e4m3_f16(bsw[t][c] & 0xFFu);
-      bsc[t][c][1] = e4m3_f16(bsw[t][c] >> 8);
-    }
+    for (int c = 0; c < 2; ++c) bsc[t][c] = e4m3x2_f16(bsw[t][c]);
 #pragma unroll
-  for (int i = 0; i < SL; ++i) {
-    asc[i][0] = e4m3_f16(asw[i] & 0xFFu);
-    asc[i][1] = e4m3_f16(asw[i] >> 8);
-  }
+  for (int i = 0; i < SL; ++i) asc[i] = e4m3x2_f16(asw[i]);
   half8_t B[NTW][8];
   // B unit m feeds MFMA m of the first row tile: K slice j = m / NTW of
   // expert tile t = m % NTW.
   auto bunit = [&](auto uc) {
     constexpr int m = decltype(uc)::value, j = m / NTW, t = m % NTW;
-    B[t][j] = fp4x8_scaled(Rc.b[t][j / 4][j % 4], bsc[t][j / 4][(j % 4) >> 1]);
+    B[t][j] = fp4x8_scaled(Rc.b[t][j / 4][j % 4], bsc[t][j / 4], (j % 4) >> 1);
   };
   auto aunit = [&](auto uc) {
     constexpr int i = decltype(uc)::value / 4, q = decltype(uc)::value % 4;
     const int row = (tid >> 2) + 64 * i;
     if (BM >= 64 || row < BM)  // BM = 32: threads 128..255 hold no row
-      reinterpret_cast<half8_t*>(abuf_n + row * kMmaARow + 32 * q4)[q] = fp4x8_scaled(Rn.a[i][q], asc[i][q >> 1]);
+      reinterpret_cast<half8_t*>(abuf_n + row * kMmaARow + 32 * q4)[q] = fp4x8_scaled(Rn.a[i][q], asc[i], q >> 1);
   };
   const _Float16* arow = abuf + r * kMmaARow + 32 * h;
   auto afrag = [&](int rt, int j) {
@@ -329,7 +347,9 @@ __device__ __forceinline__ void mma_mainloop(const MmaPtrs<BM, NTW>& P, int D, i
   constexpr int NS = mma_sets<BM, NTW>(), SL = mma_row_slots<BM>();
   constexpr int RING = mma_ring<BM, NTW>(), SPI = KS * RING, IPW = kMmaWin / SPI, POS = IPW * RING;
   static_assert(kMmaWin % SPI == 0, "a window holds whole ring passes");
-  const int grp = (threadIdx.x >> 6) >> 2;
+  // The K group as a scalar, so that step indexes (and the staged loads'
+  // scalar offsets) stay scalar.
+  const int grp = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 8));
   const int tid = threadIdx.x & (kMmaThreads - 1), q4 = tid & 3, r = lane & 31, h = lane >> 5;
   const int rows = D / 16;
   auto abuf = [&](int i) { return abuf_base + (2 * grp + i) * (BM * kMmaARow); };
