@@ -111,6 +111,8 @@ def synth(shape, seed, scale=1.0):
     (2, 2, 16384, 70),     # GEMV path: largest D it takes, eight chunks per lane
     (4, 1, 4128, 64),      # GEMV path: the last chunk of each lane's row ragged
     (2, 5, 512, 96),       # five rows per group: the MFMA path again
+    (2, 40, 2304, 136),    # 18 K steps: scale windows of 8 steps, the last one partial
+    (3, 130, 2560, 130),   # 128-row tiles over 20 K steps (three windows), ragged rows and columns
 ])
 def test_grouped_shapes(dev, ws, G, P, D, N):
     log(f"grouped G={G} P={P} D={D} N={N}")

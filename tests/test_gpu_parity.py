@@ -339,6 +339,8 @@ def synth(shape, seed, scale=1.0):
     (640, 384, 200, 8),    # MFMA gate, experts split over workgroups, second block partly empty
     (512, 512, 512, 32),   # MFMA gate, largest E and k
     (8200, 256, 256, 8),   # split experts, ragged last token block
+    (300, 2304, 256, 8),   # MFMA gate, 18 K steps: scale windows of 8 steps, the last one partial
+    (700, 3328, 384, 8),   # one K group, 26 K steps (four windows), E not a multiple of 256
     (300, 256, 64, 4),     # MFMA gate with fewer experts than one expert block (64 of 128 columns)
     (600, 512, 16, 2),     # likewise, 16 experts
     (2, 7168, 100, 8),     # decode gate: E not a multiple of 16
