@@ -265,8 +265,8 @@ constexpr int mma_ksplit() {
 }
 
 // One step: the MFMAs of step s with A from the LDS tile and B converted
-// from this step's raw chunks (Rc) just ahead of the MFMAs of the first row
-// tile that use it, interleaved with the conversion of step s + 1's A
+// from this step's raw chunks (Rc) a few units ahead of the MFMAs of the
+// first row tile that use it, interleaved with the conversion of step s + 1's A
 // chunks (Rn) into the other LDS tile. A wavefront issues one instruction
 // every few clocks while an MFMA keeps the matrix core busy for 32, so each
 // MFMA is followed by a share of the conversion units (8 elements each) and,
@@ -313,14 +313,18 @@ __device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& Rc, const uint3
   half8_t A[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) A[j] = afrag(0, j);
-  bunit(IntC<0>{});
+  // The first NPRE B units go ahead of the first MFMA, into the wait for
+  // the step's first A fragments (the A tile was stored before the barrier
+  // just passed): measured 3-5 % faster than one.
+  constexpr int NPRE = NB < 4 ? NB : 4;
+  static_for<0, NPRE>(bunit);
   static_for<0, NM>([&](auto mc) {
     constexpr int m = decltype(mc)::value;
     constexpr int rt = m / (8 * NTW), j = (m / NTW) % 8, t = m % NTW;
     f32x16_t& c = acc[NS == 2 ? (j >> 2) : 0][rt][t];
     c = mfma32(A[j], B[t][j], c);
     if constexpr (t == NTW - 1 && rt + 1 < BM / 32) A[j] = afrag(rt + 1, j);
-    if constexpr (m + 1 < NB) bunit(IntC<m + 1>{});
+    if constexpr (m + NPRE < NB) bunit(IntC<m + NPRE>{});
     static_for<(m * NA + NM - 1) / NM, ((m + 1) * NA + NM - 1) / NM>(aunit);
     if constexpr (mma_ksplit<BM, NTW>() == 2) __builtin_amdgcn_sched_barrier(0);
   });
