@@ -156,51 +156,61 @@ __global__ __launch_bounds__(kGvThreads) void grouped_gemv_kernel(GroupedArgs a,
 
   const float scale = gsa * gsw;
   const int col_base = ct * kGvCols + wave * kGvRowsPerWave;
-  const uint8_t* wcg = a.wc + (int64_t)g * a.N * rowc;
-  const uint8_t* wsg = a.ws + (int64_t)g * a.N * rows;
-  for (int u0 = 0; u0 < kGvRowsPerWave; u0 += kGvInFlight) {
-    u32x4_t wv[kGvInFlight][CPL];
-    uint32_t wsv[kGvInFlight][CPL];
+  // Raw buffer loads over group g's weights: a row past N reads zeros, and a
+  // chunk past D gets an offset past the range (zeros, no branch), so the
+  // loads are unconditional and complete in issue order.
+  const __amdgpu_buffer_rsrc_t wcr = make_rsrc(a.wc + (int64_t)g * a.N * rowc, (int64_t)a.N * rowc);
+  const __amdgpu_buffer_rsrc_t wsr = make_rsrc(a.ws + (int64_t)g * a.N * rows, (int64_t)a.N * rows);
+  uint32_t oc[CPL], os[CPL];
 #pragma unroll
-    for (int u = 0; u < kGvInFlight; ++u) {
-      const int n = col_base + u0 + u;
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    oc[i] = c < nch ? (uint32_t)(16 * c) : kMmaOob;
+    os[i] = c < nch ? (uint32_t)(2 * c) : kMmaOob;
+  }
+  u32x4_t wv[kGvInFlight][CPL];
+  uint32_t wsv[kGvInFlight][CPL];
+  auto load_row = [&](int slot, int u) {
+    const int n = col_base + u;
+    const uint32_t rc = (uint32_t)n * (uint32_t)rowc, rs = (uint32_t)n * (uint32_t)rows;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = lane + 64 * i;
-        const bool ok = n < a.N && c < nch;
-        const u32x4_t* pc = reinterpret_cast<const u32x4_t*>(wcg + (int64_t)n * rowc + 16 * c);
-        const uint16_t* ps = reinterpret_cast<const uint16_t*>(wsg + (int64_t)n * rows + 2 * c);
-        wv[u][i] = ok ? __builtin_nontemporal_load(pc) : u32x4_t{0u, 0u, 0u, 0u};
-        wsv[u][i] = ok ? __builtin_nontemporal_load(ps) : 0u;
-      }
+    for (int i = 0; i < CPL; ++i) {
+      wv[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wcr, oc[i] + rc, 0, kNtAux));
+      wsv[slot][i] = __builtin_amdgcn_raw_buffer_load_b16(wsr, os[i] + rs, 0, kNtAux);
     }
+  };
+  // A ring of kGvInFlight rows: row u + kGvInFlight is loaded into row u's
+  // registers as soon as row u is summed, so that many rows stay in flight
+  // throughout (loads complete in order: summing row u waits for its own).
 #pragma unroll
-    for (int u = 0; u < kGvInFlight; ++u) {
-      const int n = col_base + u0 + u;
-      float acc[kGvMaxRows];
+  for (int u = 0; u < kGvInFlight; ++u) load_row(u, u);
 #pragma unroll
-      for (int t = 0; t < kGvMaxRows; ++t) acc[t] = 0.0f;
+  for (int u = 0; u < kGvRowsPerWave; ++u) {
+    const int slot = u % kGvInFlight, n = col_base + u;
+    float acc[kGvMaxRows];
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = min(lane + 64 * i, nch - 1);  // chunks past D hold zero weights
-        const _Float16 s0 = e4m3_f16(wsv[u][i] & 0xFFu), s1 = e4m3_f16(wsv[u][i] >> 8);
-        const half8_t w0 = fp4x8_to_f16(wv[u][i][0], s0), w1 = fp4x8_to_f16(wv[u][i][1], s0);
-        const half8_t w2 = fp4x8_to_f16(wv[u][i][2], s1), w3 = fp4x8_to_f16(wv[u][i][3], s1);
+    for (int t = 0; t < kGvMaxRows; ++t) acc[t] = 0.0f;
 #pragma unroll
-        for (int t = 0; t < kGvMaxRows; ++t) {
-          if (t < nr) {
-            const half8_t* xp = xg + (int64_t)t * (nch * 4) + 4 * c;
-            acc[t] += dot8(xp[1], w1, dot8(xp[0], w0, 0.0f));
-            acc[t] += dot8(xp[3], w3, dot8(xp[2], w2, 0.0f));
-          }
-        }
-      }
+    for (int i = 0; i < CPL; ++i) {
+      const int c = min(lane + 64 * i, nch - 1);  // chunks past D hold zero weights
+      const _Float16 s0 = e4m3_f16(wsv[slot][i] & 0xFFu), s1 = e4m3_f16(wsv[slot][i] >> 8);
+      const half8_t w0 = fp4x8_to_f16(wv[slot][i][0], s0), w1 = fp4x8_to_f16(wv[slot][i][1], s0);
+      const half8_t w2 = fp4x8_to_f16(wv[slot][i][2], s1), w3 = fp4x8_to_f16(wv[slot][i][3], s1);
 #pragma unroll
       for (int t = 0; t < kGvMaxRows; ++t) {
         if (t < nr) {
-          const float y = wave_sum(acc[t]) * scale;
-          if (lane == 0 && n < a.N) a.out[(int64_t)(r_begin + t) * a.N + n] = y;
+          const half8_t* xp = xg + (int64_t)t * (nch * 4) + 4 * c;
+          acc[t] += dot8(xp[1], w1, dot8(xp[0], w0, 0.0f));
+          acc[t] += dot8(xp[3], w3, dot8(xp[2], w2, 0.0f));
         }
+      }
+    }
+    if (u + kGvInFlight < kGvRowsPerWave) load_row(slot, u + kGvInFlight);
+#pragma unroll
+    for (int t = 0; t < kGvMaxRows; ++t) {
+      if (t < nr) {
+        const float y = wave_sum(acc[t]) * scale;
+        if (lane == 0 && n < a.N) a.out[(int64_t)(r_begin + t) * a.N + n] = y;
       }
     }
   }

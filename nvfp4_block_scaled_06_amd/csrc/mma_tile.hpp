@@ -99,6 +99,7 @@ struct MmaRegs {
 // counters of the load ring stay exact. Offsets are per lane; a step adds 64
 // code bytes and 8 scale bytes.
 constexpr uint32_t kMmaOob = 0x80000000u;  // beyond every descriptor's range
+constexpr int kNtAux = 2;                  // raw buffer load cache policy: nontemporal (streaming)
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
