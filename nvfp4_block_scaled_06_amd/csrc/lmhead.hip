@@ -10,8 +10,10 @@
 // the bandwidth, not the launch and handoff latency, sets the time.
 //
 //  * Workgroup: 64 rows, four wavefronts of 16 rows, 4 rows in flight per
-//    wavefront; lane l takes the 32-element chunks l, l + 64, ... of a row
-//    (16 code bytes and 2 scale bytes each, coalesced 1 KB per wavefront).
+//    wavefront at all times (a rolling ring: a row's loads are issued as soon
+//    as the row four before it is summed); lane l takes the 32-element chunks
+//    l, l + 64, ... of a row (16 code bytes and 2 scale bytes each, coalesced
+//    1 KB per wavefront).
 //    The weights are read once per call, with nontemporal loads (measured:
 //    110 us against 115 us with cached loads at 129,280 x 7168; 8 rows in
 //    flight or 8 rows per wavefront were no faster).
@@ -23,7 +25,7 @@
 //    workspace with a device-coherent store; the last workgroup to arrive
 //    (arrival counter) takes the maximum over them.
 #include "../../include/nvfp4_router.h"
-#include "gate_common.hpp"
+#include "mma_tile.hpp"  // gate_common.hpp, raw buffer descriptors
 
 namespace nvr {
 
@@ -98,55 +100,66 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_argmax_kernel(LmArgs a) {
 #pragma unroll
   for (int t = 0; t < kLmMaxT; ++t) best[t] = 0ull;
   const int row_base = blockIdx.x * kLmRows + wave * kLmRowsPerWave;
-  for (int g = 0; g < kLmRowsPerWave; g += kLmInFlight) {
-    // Loads of kLmInFlight rows first. Chunks past D or rows past N load
-    // zeros and contribute nothing (their x chunk index is clamped).
-    u32x4_t wv[kLmInFlight][CPL];
-    uint32_t wsv[kLmInFlight][CPL];
+  // Raw buffer loads over the weights: rows past N read zeros, and chunks
+  // past D get an offset past the range (zeros, no branch), so the loads are
+  // unconditional and complete in issue order. A ring of kLmInFlight rows:
+  // row u + kLmInFlight is loaded into row u's registers as soon as row u is
+  // summed, so that many rows stay in flight throughout (summing row u waits
+  // for its own loads only). Rows past N and chunks past D contribute
+  // nothing (their x chunk index is clamped).
+  const __amdgpu_buffer_rsrc_t wcr = make_rsrc(a.wc, (int64_t)a.N * rowc);
+  const __amdgpu_buffer_rsrc_t wsr = make_rsrc(a.ws, (int64_t)a.N * rows);
+  uint32_t oc[CPL], os[CPL];
 #pragma unroll
-    for (int u = 0; u < kLmInFlight; ++u) {
-      const int row = row_base + g + u;
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    oc[i] = c < nch ? (uint32_t)(16 * c) : kMmaOob;
+    os[i] = c < nch ? (uint32_t)(2 * c) : kMmaOob;
+  }
+  u32x4_t wv[kLmInFlight][CPL];
+  uint32_t wsv[kLmInFlight][CPL];
+  auto load_row = [&](int slot, int u) {
+    const int row = row_base + u;
+    const uint32_t rc = (uint32_t)row * (uint32_t)rowc, rs = (uint32_t)row * (uint32_t)rows;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = lane + 64 * i;
-        const bool ok = row < a.N && c < nch;
-        const u32x4_t* pc = reinterpret_cast<const u32x4_t*>(a.wc + (int64_t)row * rowc + 16 * c);
-        const uint16_t* ps = reinterpret_cast<const uint16_t*>(a.ws + (int64_t)row * rows + 2 * c);
-        wv[u][i] = ok ? __builtin_nontemporal_load(pc) : u32x4_t{0u, 0u, 0u, 0u};
-        wsv[u][i] = ok ? __builtin_nontemporal_load(ps) : 0u;
-      }
+    for (int i = 0; i < CPL; ++i) {
+      wv[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wcr, oc[i] + rc, 0, kNtAux));
+      wsv[slot][i] = __builtin_amdgcn_raw_buffer_load_b16(wsr, os[i] + rs, 0, kNtAux);
     }
+  };
 #pragma unroll
-    for (int u = 0; u < kLmInFlight; ++u) {
-      const int row = row_base + g + u;
-      float acc[kLmMaxT];
+  for (int u = 0; u < kLmInFlight; ++u) load_row(u, u);
 #pragma unroll
-      for (int t = 0; t < kLmMaxT; ++t) acc[t] = 0.0f;
+  for (int u = 0; u < kLmRowsPerWave; ++u) {
+    const int slot = u % kLmInFlight, row = row_base + u;
+    float acc[kLmMaxT];
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = min(lane + 64 * i, nch - 1);
-        const _Float16 s0 = e4m3_f16(wsv[u][i] & 0xFFu), s1 = e4m3_f16(wsv[u][i] >> 8);
-        const half8_t w0 = fp4x8_to_f16(wv[u][i][0], s0), w1 = fp4x8_to_f16(wv[u][i][1], s0);
-        const half8_t w2 = fp4x8_to_f16(wv[u][i][2], s1), w3 = fp4x8_to_f16(wv[u][i][3], s1);
+    for (int t = 0; t < kLmMaxT; ++t) acc[t] = 0.0f;
 #pragma unroll
-        for (int t = 0; t < kLmMaxT; ++t) {
-          if (t < T) {
-            const half8_t* xp = xl + (int64_t)t * (nch * 4) + 4 * c;
-            // One block (two halves) at a time: exact block sums, then fp32 accumulation.
-            acc[t] += dot8(xp[1], w1, dot8(xp[0], w0, 0.0f));
-            acc[t] += dot8(xp[3], w3, dot8(xp[2], w2, 0.0f));
-          }
-        }
-      }
+    for (int i = 0; i < CPL; ++i) {
+      const int c = min(lane + 64 * i, nch - 1);
+      const _Float16 s0 = e4m3_f16(wsv[slot][i] & 0xFFu), s1 = e4m3_f16(wsv[slot][i] >> 8);
+      const half8_t w0 = fp4x8_to_f16(wv[slot][i][0], s0), w1 = fp4x8_to_f16(wv[slot][i][1], s0);
+      const half8_t w2 = fp4x8_to_f16(wv[slot][i][2], s1), w3 = fp4x8_to_f16(wv[slot][i][3], s1);
 #pragma unroll
       for (int t = 0; t < kLmMaxT; ++t) {
         if (t < T) {
-          const float L = (float)((double)wave_sum(acc[t]) * scale);
-          if (row < a.N) {
-            const uint64_t key = ((uint64_t)score_key(L) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)row);
-            best[t] = key > best[t] ? key : best[t];
-            if (a.logits_out && lane == 0) a.logits_out[(int64_t)t * a.N + row] = L;
-          }
+          const half8_t* xp = xl + (int64_t)t * (nch * 4) + 4 * c;
+          // One block (two halves) at a time: exact block sums, then fp32 accumulation.
+          acc[t] += dot8(xp[1], w1, dot8(xp[0], w0, 0.0f));
+          acc[t] += dot8(xp[3], w3, dot8(xp[2], w2, 0.0f));
+        }
+      }
+    }
+    if (u + kLmInFlight < kLmRowsPerWave) load_row(slot, u + kLmInFlight);
+#pragma unroll
+    for (int t = 0; t < kLmMaxT; ++t) {
+      if (t < T) {
+        const float L = (float)((double)wave_sum(acc[t]) * scale);
+        if (row < a.N) {
+          const uint64_t key = ((uint64_t)score_key(L) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)row);
+          best[t] = key > best[t] ? key : best[t];
+          if (a.logits_out && lane == 0) a.logits_out[(int64_t)t * a.N + row] = L;
         }
       }
     }
