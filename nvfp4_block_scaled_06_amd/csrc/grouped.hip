@@ -156,11 +156,14 @@ __global__ __launch_bounds__(kGvThreads) void grouped_gemv_kernel(GroupedArgs a,
 
   const float scale = gsa * gsw;
   const int col_base = ct * kGvCols + wave * kGvRowsPerWave;
-  // Raw buffer loads over group g's weights: a row past N reads zeros, and a
+  // Raw buffer loads over this workgroup's weight rows of group g (32-bit
+  // ranges and offsets then hold for any N): a row past N reads zeros, and a
   // chunk past D gets an offset past the range (zeros, no branch), so the
   // loads are unconditional and complete in issue order.
-  const __amdgpu_buffer_rsrc_t wcr = make_rsrc(a.wc + (int64_t)g * a.N * rowc, (int64_t)a.N * rowc);
-  const __amdgpu_buffer_rsrc_t wsr = make_rsrc(a.ws + (int64_t)g * a.N * rows, (int64_t)a.N * rows);
+  const int64_t wg_row0 = (int64_t)g * a.N + (int64_t)ct * kGvCols;
+  const int64_t wg_rows = min((int64_t)kGvCols, (int64_t)a.N - (int64_t)ct * kGvCols);
+  const __amdgpu_buffer_rsrc_t wcr = make_rsrc(a.wc + wg_row0 * rowc, wg_rows * rowc);
+  const __amdgpu_buffer_rsrc_t wsr = make_rsrc(a.ws + wg_row0 * rows, wg_rows * rows);
   uint32_t oc[CPL], os[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
@@ -171,8 +174,8 @@ __global__ __launch_bounds__(kGvThreads) void grouped_gemv_kernel(GroupedArgs a,
   u32x4_t wv[kGvInFlight][CPL];
   uint32_t wsv[kGvInFlight][CPL];
   auto load_row = [&](int slot, int u) {
-    const int n = col_base + u;
-    const uint32_t rc = (uint32_t)n * (uint32_t)rowc, rs = (uint32_t)n * (uint32_t)rows;
+    const int lr = wave * kGvRowsPerWave + u;  // weight row within the workgroup
+    const uint32_t rc = (uint32_t)lr * (uint32_t)rowc, rs = (uint32_t)lr * (uint32_t)rows;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       wv[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wcr, oc[i] + rc, 0, kNtAux));

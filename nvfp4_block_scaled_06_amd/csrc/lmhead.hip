@@ -100,15 +100,19 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_argmax_kernel(LmArgs a) {
 #pragma unroll
   for (int t = 0; t < kLmMaxT; ++t) best[t] = 0ull;
   const int row_base = blockIdx.x * kLmRows + wave * kLmRowsPerWave;
-  // Raw buffer loads over the weights: rows past N read zeros, and chunks
+  // Raw buffer loads: rows past N read zeros, and chunks
   // past D get an offset past the range (zeros, no branch), so the loads are
   // unconditional and complete in issue order. A ring of kLmInFlight rows:
   // row u + kLmInFlight is loaded into row u's registers as soon as row u is
   // summed, so that many rows stay in flight throughout (summing row u waits
   // for its own loads only). Rows past N and chunks past D contribute
   // nothing (their x chunk index is clamped).
-  const __amdgpu_buffer_rsrc_t wcr = make_rsrc(a.wc, (int64_t)a.N * rowc);
-  const __amdgpu_buffer_rsrc_t wsr = make_rsrc(a.ws, (int64_t)a.N * rows);
+  // Descriptors over this workgroup's rows only (from its first row): 32-bit
+  // ranges and offsets then hold for any N.
+  const int64_t wg_row0 = (int64_t)blockIdx.x * kLmRows;
+  const int64_t wg_rows = min((int64_t)kLmRows, (int64_t)a.N - wg_row0);
+  const __amdgpu_buffer_rsrc_t wcr = make_rsrc(a.wc + wg_row0 * rowc, wg_rows * rowc);
+  const __amdgpu_buffer_rsrc_t wsr = make_rsrc(a.ws + wg_row0 * rows, wg_rows * rows);
   uint32_t oc[CPL], os[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
@@ -119,8 +123,8 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_argmax_kernel(LmArgs a) {
   u32x4_t wv[kLmInFlight][CPL];
   uint32_t wsv[kLmInFlight][CPL];
   auto load_row = [&](int slot, int u) {
-    const int row = row_base + u;
-    const uint32_t rc = (uint32_t)row * (uint32_t)rowc, rs = (uint32_t)row * (uint32_t)rows;
+    const int lr = wave * kLmRowsPerWave + u;  // row within the workgroup
+    const uint32_t rc = (uint32_t)lr * (uint32_t)rowc, rs = (uint32_t)lr * (uint32_t)rows;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       wv[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wcr, oc[i] + rc, 0, kNtAux));

@@ -13,7 +13,7 @@ import torch
 
 from nvfp4_block_scaled_06_amd import router as rt
 from nvfp4_block_scaled_06_amd import workloads as wl
-from oracle import check, lmhead_ref, router_ref
+from oracle import check, lmhead_ref, quant_ref, router_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -99,7 +99,7 @@ def test_lmhead_full_vocabulary_sampled(dev):
     log(f"lmhead full size N={N}")
     ws = workspace(dev, T, D, N)
     g = torch.Generator(device=dev).manual_seed(1234)
-    w = (torch.randn((N, D), generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    w = torch.randn((N, D), generator=g, device=dev, dtype=torch.bfloat16)
     wq = quantize_dev(w, ws)
     del w
     x_bits = synth_bits((T, D), 4321, 1.0)
@@ -117,3 +117,40 @@ def test_lmhead_full_vocabulary_sampled(dev):
     sel = np.searchsorted(rows, idx)
     fails += lmhead_ref.check_argmax(np.array([sel]), np.array([logit]), L, A)
     assert not fails, "\n".join(fails[:10])
+
+
+@pytest.mark.gpu
+def test_lmhead_weights_past_32bit_offsets(dev):
+    """N x D/2 code bytes above 2^32 (4.3 GB, past any 32-bit byte offset from the matrix's start): the loads'
+    buffer ranges and offsets are per workgroup, so rows far into the matrix read their own bytes. The oracle on
+    sampled rows, the last 64 rows and the 33 rows with the largest device logits."""
+    T, D, N = 1, 16384, (1 << 19) + 3
+    assert N * D // 2 > (1 << 32)
+    log(f"lmhead N={N} D={D}: {N * D // 2} code bytes")
+    ws = workspace(dev, T, D, N)
+    g = torch.Generator(device=dev).manual_seed(77)
+    w = torch.randn((N, D), generator=g, device=dev, dtype=torch.bfloat16)
+    wq = quantize_dev(w, ws)
+    x_bits = synth_bits((T, D), 7654, 1.0)
+    xq = quantize_dev(to_dev(x_bits, dev), ws)
+    idx, logit, logits = rt.lmhead_argmax(xq, wq, ws, want_logits=True)
+    torch.cuda.synchronize()
+    idx, logit, Lg = int(idx.cpu()[0]), float(logit.cpu()[0]), logits.cpu().numpy()[0]
+    assert idx == int(np.argmax(Lg)) and logit == float(Lg[idx])
+    rows = np.unique(np.concatenate([wl.sample_rows(N, 128, seed=9), np.arange(N - 64, N),
+                                     np.argsort(-Lg)[:33]]))
+    ri = torch.from_numpy(rows).to(dev)
+    # Codes of the sampled rows against the oracle's under the device's global scale, whose value is checked
+    # against the tensor's max on its own.
+    wc, wsb, gsw = wq.codes[ri].cpu().numpy(), wq.scales[ri].cpu().numpy(), wq.gscale.cpu().numpy()[0]
+    amax = float(w.abs().max().float().cpu())
+    assert gsw == quant_ref.gsa_ref(amax)
+    wr = quant_ref.quantize_ref(w[ri].view(torch.int16).cpu().numpy().view(np.uint16), gsa_override=gsw)
+    del w
+    fails = check.check_quant(wc, wsb, gsw, wr)
+    L, A = router_ref.logits_ref(*host(xq), wc, wsb, gsw)
+    fails += check.check_logits(Lg[rows][None, :], L, A)
+    sel = np.searchsorted(rows, idx)
+    fails += lmhead_ref.check_argmax(np.array([sel]), np.array([logit]), L, A)
+    assert not fails, "\n".join(fails[:10])
+
