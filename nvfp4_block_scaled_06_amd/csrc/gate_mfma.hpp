@@ -4,6 +4,7 @@
 #pragma once
 
 #include "mma_tile.hpp"
+#include "route16.hpp"
 
 namespace nvr {
 
@@ -56,12 +57,14 @@ struct MmaArgs {
   int nsteps;  // 128-element K steps, rounded up to whole scale windows
 };
 
-// Epilogue rows per pass: 64 when two K groups share the work and the rows
-// fit the LDS, else 32. Each wavefront routes LR / (4 KS) rows per pass, as
-// sets of four, two sets per call (interleaved, for latency hiding: with one
-// wavefront per SIMD this was worth ~6 % of the large-prefill gate).
+// Epilogue rows per pass: 64 when the tile has them and their logits rows
+// fit the LDS (up to 384 experts), else 32 (fewer passes: measured 2-3 %
+// of the large-prefill gate with one K group). Each wavefront routes
+// LR / (4 KS) rows per pass, as sets of four, two sets per call
+// (interleaved, for latency hiding: with one wavefront per SIMD this was
+// worth ~6 % of the large-prefill gate).
 template <int BM, int J16, int KS>
-constexpr int epi_rows() { return KS == 2 && BM >= 64 && J16 <= 24 ? 64 : 32; }
+constexpr int epi_rows() { return BM >= 64 && J16 <= 24 ? 64 : 32; }
 template <int BM, int J16, int KS>
 constexpr int epi_sets() { return KS == 2 ? epi_rows<BM, J16, KS>() / 32 : 2; }
 

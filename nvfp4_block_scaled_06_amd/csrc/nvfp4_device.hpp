@@ -565,255 +565,4 @@ __device__ __forceinline__ void wave_route_row(const float* Lrow, const float* b
   wave_route_regs<JMAX>(L, bv, E, k, routed_scale, out_idx, out_w, sc);
 }
 
-// Throughput routing for many tokens: 16 lanes (one DPP row) per token, four
-// tokens per wavefront at once. Same six steps, selection rule and order as
-// wave_route_regs. Lane l of a row holds the J16 consecutive experts
-// l J16 .. l J16 + J16 - 1, read with 16-byte LDS loads (rows of logits and
-// the bias must be readable up to 16 J16 entries).
-//  1. keys as in wave_route_regs; lm = the lane's largest key;
-//  2. for k <= 16 the k-th largest of the 16 lane maxima is a lower bound on
-//     the k-th largest key (k distinct experts reach it). Each lane counts
-//     the lanes above it over 15 DPP row rotations; the bound is the smallest
-//     lane maximum with fewer than k lanes above it. Everything at or above
-//     it survives: usually k or a few more;
-//  3. for k > 16, or when more than 32 survive (flat or tied scores), the
-//     exact k-th largest key K is found bit by bit from the top (32 row
-//     counts of keys >= t); the survivors are then the keys above K plus the
-//     lowest-index experts whose key equals K, exactly k of them;
-//  4. the survivors (at most 32) are compacted by a row prefix sum and each
-//     is ranked against all of them with one batch of LDS reads; the weight
-//     sum is a DPP row sum and each chosen lane stores its output at its rank.
-constexpr int kRow16MaxSurvivors = 32;
-
-// Entry kRow16MaxSurvivors of each row is a spare slot that absorbs the
-// writes of non-surviving keys, so compaction needs no branch per key. One
-// scratch serves NSET sets of four rows.
-template <int J16, int NSET>
-struct Row16Scratch {
-  uint64_t cand[NSET][4][kRow16MaxSurvivors + 1];
-  float cs[NSET][4][kRow16MaxSurvivors + 1];
-};
-
-__device__ __forceinline__ uint32_t row_min_u32(uint32_t v) {
-  v = min(v, dpp_u<kDppXor1>(v));
-  v = min(v, dpp_u<kDppXor2>(v));
-  v = min(v, dpp_u<kDppHalfMirror>(v));
-  v = min(v, dpp_u<kDppMirror>(v));
-  return v;
-}
-
-__device__ __forceinline__ float row_sum(float v) {
-  v += __int_as_float(dpp_i<kDppXor1>(__float_as_int(v)));
-  v += __int_as_float(dpp_i<kDppXor2>(__float_as_int(v)));
-  v += __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(v)));
-  v += __int_as_float(dpp_i<kDppMirror>(__float_as_int(v)));
-  return v;
-}
-
-__device__ __forceinline__ int row_sum_i(int v) {
-  v += dpp_i<kDppXor1>(v);
-  v += dpp_i<kDppXor2>(v);
-  v += dpp_i<kDppHalfMirror>(v);
-  v += dpp_i<kDppMirror>(v);
-  return v;
-}
-
-// Inclusive prefix sum over the 16 lanes of each DPP row.
-__device__ __forceinline__ int row_scan(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
-  return v;
-}
-
-// Number of lanes of the row whose value exceeds this lane's (row_ror:R).
-template <int R>
-__device__ __forceinline__ int count_above(uint32_t v, int n) {
-  if constexpr (R < 16) return count_above<R + 1>(v, n + (dpp_u<0x120 + R>(v) > v ? 1 : 0));
-  return n;
-}
-
-// Survivors 0..NS-1 of each row (entries past the count are zero), ranked
-// and stored; NS = 16 or 32, lane l16 takes survivors l16 and l16 + 16.
-template <int J16, int NSET, int NS>
-__device__ __forceinline__ void row16_rank_store(const int (&C)[NSET], int k, float routed_scale,
-                                                 const bool (&valid)[NSET], int l16, int rq,
-                                                 int32_t* const (&out_idx)[NSET], float* const (&out_w)[NSET],
-                                                 const Row16Scratch<J16, NSET>& sc) {
-  uint64_t mine[NSET][NS / 16];
-  float ms[NSET][NS / 16];
-  int rank[NSET][NS / 16];
-#pragma unroll
-  for (int r = 0; r < NSET; ++r)
-#pragma unroll
-    for (int h = 0; h < NS / 16; ++h) {
-      mine[r][h] = sc.cand[r][rq][l16 + 16 * h];
-      ms[r][h] = sc.cs[r][rq][l16 + 16 * h];
-      rank[r][h] = 0;
-    }
-#pragma unroll
-  for (int u = 0; u < NS; ++u)
-#pragma unroll
-    for (int r = 0; r < NSET; ++r) {
-      const uint64_t other = sc.cand[r][rq][u];
-#pragma unroll
-      for (int h = 0; h < NS / 16; ++h) rank[r][h] += other > mine[r][h] ? 1 : 0;
-    }
-  float part[NSET];
-  bool chosen[NSET][NS / 16];
-#pragma unroll
-  for (int r = 0; r < NSET; ++r) {
-    part[r] = 0.0f;
-#pragma unroll
-    for (int h = 0; h < NS / 16; ++h) {
-      chosen[r][h] = l16 + 16 * h < C[r] && rank[r][h] < k;
-      part[r] += chosen[r][h] ? ms[r][h] : 0.0f;
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < NSET; ++r) {
-    const float f = routed_scale * __builtin_amdgcn_rcpf(row_sum(part[r]));
-#pragma unroll
-    for (int h = 0; h < NS / 16; ++h)
-      if (valid[r] && chosen[r][h]) {
-        out_idx[r][rank[r][h]] = (int)(0xFFFFFFFFu - (uint32_t)mine[r][h]);
-        out_w[r][rank[r][h]] = ms[r][h] * f;
-      }
-  }
-}
-
-// Largest per-row survivor count over the four rows of every set.
-template <int NSET>
-__device__ __forceinline__ int rows_max(const int (&C)[NSET]) {
-  int m = 0;
-#pragma unroll
-  for (int r = 0; r < NSET; ++r)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) m = max(m, (int)__builtin_amdgcn_readlane(C[r], 16 * q));
-  return m;
-}
-
-// Routes NSET independent sets of four rows at once (lane l16 of row group
-// rq of set r reads Lrow[r]); the sets' instruction streams interleave, which
-// hides the latency of each set's dependent steps.
-template <int J16, int NSET>
-__device__ __forceinline__ void row16_route(const float* const (&Lrow)[NSET], const float* bias_lds, int E, int k,
-                                            float routed_scale, const bool (&valid)[NSET],
-                                            int32_t* const (&out_idx)[NSET], float* const (&out_w)[NSET],
-                                            Row16Scratch<J16, NSET>& sc) {
-  const int lane = threadIdx.x & 63, l16 = lane & 15, rq = lane >> 4;
-  const int e0 = l16 * J16;
-  uint32_t key[NSET][J16];
-  float s[NSET][J16];
-  uint32_t lm[NSET];
-#pragma unroll
-  for (int r = 0; r < NSET; ++r) lm[r] = 0u;
-#pragma unroll
-  for (int j4 = 0; j4 < J16 / 4; ++j4) {
-    const float4 B4 = *reinterpret_cast<const float4*>(bias_lds + e0 + 4 * j4);
-    const float Bv[4] = {B4.x, B4.y, B4.z, B4.w};
-#pragma unroll
-    for (int r = 0; r < NSET; ++r) {
-      const float4 L4 = *reinterpret_cast<const float4*>(Lrow[r] + e0 + 4 * j4);
-      const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 4 * j4 + i;
-        s[r][j] = sigmoid_fast(Lv[i]);
-        key[r][j] = (e0 + j < E && valid[r]) ? score_key(s[r][j] + Bv[i]) : 0u;
-        lm[r] = max(lm[r], key[r][j]);
-      }
-    }
-  }
-  // Survivor rule: a nonzero key > hi, or == hi among this lane's first
-  // `ties` such keys (the bound: hi = tau - 1, no ties taken; the exact
-  // search: hi = K, ties shared out in index order).
-  uint32_t hi[NSET];
-  int ties[NSET], C[NSET];
-#pragma unroll
-  for (int r = 0; r < NSET; ++r) {
-    hi[r] = 0u;
-    ties[r] = 0x7FFFFFFF;
-    C[r] = kRow16MaxSurvivors + 1;
-  }
-  if (k <= 16) {
-#pragma unroll
-    for (int r = 0; r < NSET; ++r) {
-      const int above = count_above<1>(lm[r], 0);
-      const uint32_t tau = row_min_u32(above < k ? lm[r] : 0xFFFFFFFFu);
-      int cnt = 0;
-#pragma unroll
-      for (int j = 0; j < J16; ++j) cnt += (key[r][j] != 0u && key[r][j] >= tau) ? 1 : 0;
-      C[r] = row_sum_i(cnt);
-      hi[r] = tau > 0u ? tau - 1u : 0u;  // key > hi <=> key >= tau, for the nonzero keys
-      ties[r] = 0;
-    }
-  }
-  if (rows_max<NSET>(C) > kRow16MaxSurvivors) {
-    // Exact k-th largest key K of each row, bit by bit: the largest t with at
-    // least k keys >= t.
-    uint32_t K[NSET];
-#pragma unroll
-    for (int r = 0; r < NSET; ++r) K[r] = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-#pragma unroll
-      for (int r = 0; r < NSET; ++r) {
-        const uint32_t t = K[r] | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < J16; ++j) cnt += key[r][j] >= t ? 1 : 0;
-        if (row_sum_i(cnt) >= k) K[r] = t;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < NSET; ++r) {
-      int gt = 0, eq = 0;
-#pragma unroll
-      for (int j = 0; j < J16; ++j) {
-        gt += key[r][j] > K[r] ? 1 : 0;
-        eq += (key[r][j] == K[r] && key[r][j] != 0u) ? 1 : 0;
-      }
-      hi[r] = K[r];
-      ties[r] = k - row_sum_i(gt);                 // equal keys still to take, lowest index first
-      ties[r] -= row_scan(eq) - eq;                // minus equal keys in lanes before this one
-      C[r] = k;
-    }
-  }
-  // Compact the survivors (at most 32 per row).
-#pragma unroll
-  for (int r = 0; r < NSET; ++r) {
-    int cnt = 0, teq = 0;
-    bool surv[J16];
-#pragma unroll
-    for (int j = 0; j < J16; ++j) {
-      const bool eq = key[r][j] == hi[r] && key[r][j] != 0u;
-      surv[j] = key[r][j] != 0u && (key[r][j] > hi[r] || (eq && teq < ties[r]));
-      teq += eq ? 1 : 0;
-      cnt += surv[j] ? 1 : 0;
-    }
-    int pos = row_scan(cnt) - cnt;
-#pragma unroll
-    for (int j = 0; j < J16; ++j) {
-      const int slot = surv[j] ? pos : kRow16MaxSurvivors;
-      sc.cand[r][rq][slot] = ((uint64_t)key[r][j] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(e0 + j));
-      sc.cs[r][rq][slot] = s[r][j];
-      pos += surv[j] ? 1 : 0;
-    }
-    C[r] = row_sum_i(cnt);
-  }
-  const int ns = rows_max<NSET>(C) <= 16 ? 16 : 32;
-  // Entries past the count rank below everything.
-#pragma unroll
-  for (int r = 0; r < NSET; ++r) {
-    sc.cand[r][rq][C[r] <= l16 ? l16 : kRow16MaxSurvivors] = 0ull;
-    if (ns == 32) sc.cand[r][rq][C[r] <= l16 + 16 ? l16 + 16 : kRow16MaxSurvivors] = 0ull;
-  }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (ns == 16) row16_rank_store<J16, NSET, 16>(C, k, routed_scale, valid, l16, rq, out_idx, out_w, sc);
-  else row16_rank_store<J16, NSET, 32>(C, k, routed_scale, valid, l16, rq, out_idx, out_w, sc);
-}
-
 }  // namespace nvr
