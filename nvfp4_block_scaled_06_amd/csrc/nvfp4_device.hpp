@@ -87,39 +87,41 @@ __device__ __forceinline__ uint32_t sign_codes4(const uint32_t* w) {
 
 // E2M1 code of one element, exact for every quotient q = |x| / (gsa S)
 // (gsa in [2^-80, 2^100], S > 0 or inv = 0), from the approximate quotient
-// qa = |x| * inv (within a few ulps of q), as the fp32 value that the
-// hardware conversion (round to nearest even, saturating) then maps to the
-// right code. Every E2M1 value and every rounding threshold (0.25, 0.75,
-// 1.25, 1.75, 2.5, 3.5, 5) has at most two explicit mantissa bits:
-//  1. v = the value nearest qa with at most two explicit mantissa bits.
-//     Between v and q there is no threshold other than v itself. A huge qa
-//     (a too-small static gsa) may round to +inf; then v S gsa is +inf, the
-//     residual below is -inf, v moves down to a large finite value and the
-//     conversion saturates to 6, as q does.
-//  2. r = |x| - v S gsa by one fma has the exact sign of q - v: v S is exact
-//     (at most 7 significant bits) and every term is a multiple of
-//     2^-31 v S gsa, far above the fp32 underflow threshold in this range,
-//     so the fma's one rounding cannot reach or cross zero. r is never -0
-//     (|x| >= 0, and an exact zero sum rounds to +0), so its bit pattern
-//     read as an integer and clamped to [-1, 1] is the sign of q - v.
-//  3. v moves toward q by 2^12 units in its last place (between 2^-12 v and
-//     2^-11 v; one shift-add on the bit pattern): a threshold then converts
-//     to the code on q's side, an exact tie (r = 0) stays on the threshold
-//     and converts to the even code, and any other v keeps its own code.
-//     When v = 0 (q = 0, or a zero scale with inv = 0) r >= 0, and the move
-//     gives a tiny positive value that converts to code 0.
-// The sign is copied from x last, so -0 and tiny negatives keep their sign.
+// qa = x * inv (signed, as inv >= 0; within a few ulps of +-q), as the fp32
+// value that the hardware conversion (round to nearest even on the
+// magnitude, saturating, sign kept) then maps to the right code. Every E2M1
+// value and every rounding threshold (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5)
+// has at most two explicit mantissa bits:
+//  1. v = the value nearest qa with at most two explicit mantissa bits (the
+//     rounding acts on the magnitude bits; the sign bit is kept). Between |v|
+//     and q there is no threshold other than |v| itself. A huge qa (a
+//     too-small static gsa) may round to +-inf; then |v| S gsa is +inf, the
+//     residual below is -inf, v moves toward zero to a large finite value and
+//     the conversion saturates to +-6, as q does.
+//  2. r = |x| - |v| S gsa by one fma (abs modifiers) has the exact sign of
+//     q - |v|: |v| S is exact (at most 7 significant bits) and every term is
+//     a multiple of 2^-31 |v| S gsa, far above the fp32 underflow threshold in
+//     this range, so the fma's one rounding cannot reach or cross zero. r is
+//     never -0 (|x| >= 0, and an exact zero sum rounds to +0), so its bit
+//     pattern read as an integer and clamped to [-1, 1] is the sign of
+//     q - |v|.
+//  3. |v| moves toward q by 2^12 units in its last place (between 2^-12 |v|
+//     and 2^-11 |v|; one shift-add on the bit pattern, which moves the
+//     magnitude the same way for either sign): a threshold then converts to
+//     the code on q's side, an exact tie (r = 0) stays on the threshold and
+//     converts to the even code, and any other v keeps its own code. When
+//     v = +-0 (x = +-0, or a zero scale with inv = 0) r >= 0, and the move
+//     gives a tiny value of x's sign that converts to code 0 with that sign
+//     (so -0 and tiny negatives keep their sign).
 __device__ __forceinline__ float e2m1_exact_input(float x, float inv, float S, float gsa) {
-  const float xa = fabsf(x);
-  const float qa = xa * inv;
+  const float qa = x * inv;
   const uint32_t vb = (__float_as_uint(qa) + 0x100000u) & 0xFFE00000u;
-  const float r = fmaf(-(__uint_as_float(vb) * S), gsa, xa);
+  const float r = fmaf(-(fabsf(__uint_as_float(vb)) * S), gsa, fabsf(x));
   // One v_med3_i32 (the compiler would otherwise lower the clamp to two
   // compare/select pairs).
   int sgn;
   asm("v_med3_i32 %0, %1, -1, 1" : "=v"(sgn) : "v"(__float_as_uint(r)));
-  const uint32_t wb = vb + ((uint32_t)sgn << 12);
-  return __uint_as_float((wb & 0x7FFFFFFFu) | (__float_as_uint(x) & 0x80000000u));
+  return __uint_as_float(vb + ((uint32_t)sgn << 12));
 }
 
 // One bf16 pair rounded to two E2M1 codes, written into byte I of `old`: the
