@@ -38,10 +38,12 @@ namespace nvr {
 constexpr int kMmaThreads = 256;
 
 // K steps of loads in flight: four for the small tiles, two when the
-// accumulators and weight fragments of a wide tile already need most registers.
+// accumulators and weight fragments of a wide tile already need most
+// registers (32 x 256 tiles too: two wavefronts per SIMD share the
+// registers, and the weight units stay live from one step to the next).
 template <int BM, int NTW>
 constexpr int mma_ring() {
-  return (BM / 32) * NTW >= 6 ? 2 : 4;
+  return (BM / 32) * NTW >= 6 || (BM == 32 && NTW == 2) ? 2 : 4;
 }
 constexpr int kMmaARow = 136;  // LDS row stride of the A tile in halves (128 values + 8 pad)
 
@@ -265,84 +267,139 @@ constexpr int mma_ksplit() {
   return (BM / 32) * NTW <= 2 ? 2 : 1;
 }
 
-// One step: the MFMAs of step s with A from the LDS tile and B converted
-// from this step's raw chunks (Rc) a few units ahead of the MFMAs of the
-// first row tile that use it, interleaved with the conversion of step s + 1's A
-// chunks (Rn) into the other LDS tile. A wavefront issues one instruction
-// every few clocks while an MFMA keeps the matrix core busy for 32, so each
-// MFMA is followed by a share of the conversion units (8 elements each) and,
-// in the two-group kernels, scheduling fences keep that order (measured: with
-// one K group the compiler's own order is 4 % faster at 128 tokens x 384
-// experts; with two groups the fences win). The A fragments of row tile
-// rt + 1 are read right after their last use in row tile rt.
+// Look-ahead of the A-fragment reads, in K slices (8 per step): enough that
+// the MFMAs between a read and its use cover the LDS latency.
 template <int BM, int NTW>
-__device__ __forceinline__ void mma_step(const MmaRegs<BM, NTW>& Rc, const uint32_t (&bsw)[NTW][2],
-                                         const _Float16* abuf, const MmaRegs<BM, NTW>& Rn,
-                                         const uint32_t (&asw)[mma_row_slots<BM>()], _Float16* abuf_n, int lane,
-                                         f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
-  constexpr int NS = mma_sets<BM, NTW>();
-  constexpr int SL = mma_row_slots<BM>();
-  constexpr int NM = (BM / 32) * 8 * NTW;  // MFMAs; the first 8 NTW use B units 0 .. 8 NTW - 1 in order
-  constexpr int NB = 8 * NTW;              // B units
-  constexpr int NA = 4 * SL;               // A units
-  const int r = lane & 31, h = lane >> 5;
-  const int tid = threadIdx.x & (kMmaThreads - 1), q4 = tid & 3;
-  half2_t bsc[NTW][2], asc[SL];
+constexpr int mma_afrag_ahead() {
+  return (BM / 32) * NTW >= 8 ? 2 : 4;
+}
+// A fragments in flight: [K slice mod mma_afrag_ahead()][row tile].
+template <int BM, int NTW>
+using MmaAFrags = half8_t[mma_afrag_ahead<BM, NTW>()][BM / 32];
+
+// This lane's 32-element chunks of the B rows, converted (one unit per
+// expert tile t and K slice j), from raw chunks R.b under scale words bsw.
+template <int BM, int NTW>
+__device__ __forceinline__ void mma_convert_b(half8_t (&B)[NTW][8], const MmaRegs<BM, NTW>& R,
+                                              const uint32_t (&bsw)[NTW][2]) {
 #pragma unroll
   for (int t = 0; t < NTW; ++t)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) bsc[t][c] = e4m3x2_f16(bsw[t][c]);
+    for (int c = 0; c < 2; ++c) {
+      const half2_t sc = e4m3x2_f16(bsw[t][c]);
 #pragma unroll
-  for (int i = 0; i < SL; ++i) asc[i] = e4m3x2_f16(asw[i]);
-  half8_t B[NTW][8];
-  // B unit m feeds MFMA m of the first row tile: K slice j = m / NTW of
-  // expert tile t = m % NTW.
-  auto bunit = [&](auto uc) {
-    constexpr int m = decltype(uc)::value, j = m / NTW, t = m % NTW;
-    B[t][j] = fp4x8_scaled(Rc.b[t][j / 4][j % 4], bsc[t][j / 4], (j % 4) >> 1);
-  };
-  auto aunit = [&](auto uc) {
-    constexpr int i = decltype(uc)::value / 4, q = decltype(uc)::value % 4;
-    const int row = (tid >> 2) + 64 * i;
-    if (BM >= 64 || row < BM)  // BM = 32: threads 128..255 hold no row
-      reinterpret_cast<half8_t*>(abuf_n + row * kMmaARow + 32 * q4)[q] = fp4x8_scaled(Rn.a[i][q], asc[i], q >> 1);
-  };
-  const _Float16* arow = abuf + r * kMmaARow + 32 * h;
-  auto afrag = [&](int rt, int j) {
-    return *reinterpret_cast<const half8_t*>(arow + rt * 32 * kMmaARow + (j < 4 ? 8 * j : 64 + 8 * (j - 4)));
-  };
-  half8_t A[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) A[j] = afrag(0, j);
-  // The first NPRE B units go ahead of the first MFMA, into the wait for
-  // the step's first A fragments (the A tile was stored before the barrier
-  // just passed): measured 3-5 % faster than one.
-  constexpr int NPRE = NB < 4 ? NB : 4;
-  static_for<0, NPRE>(bunit);
-  static_for<0, NM>([&](auto mc) {
-    constexpr int m = decltype(mc)::value;
-    constexpr int rt = m / (8 * NTW), j = (m / NTW) % 8, t = m % NTW;
-    f32x16_t& c = acc[NS == 2 ? (j >> 2) : 0][rt][t];
-    c = mfma32(A[j], B[t][j], c);
-    if constexpr (t == NTW - 1 && rt + 1 < BM / 32) A[j] = afrag(rt + 1, j);
-    if constexpr (m + NPRE < NB) bunit(IntC<m + NPRE>{});
-    static_for<(m * NA + NM - 1) / NM, ((m + 1) * NA + NM - 1) / NM>(aunit);
-    if constexpr (mma_ksplit<BM, NTW>() == 2) __builtin_amdgcn_sched_barrier(0);
-  });
+      for (int i = 0; i < 4; ++i) B[t][4 * c + i] = fp4x8_scaled(R.b[t][c][i], sc, i >> 1);
+    }
 }
 
+// A fragment (row tile rt, K slice j) of this lane from the step's LDS tile:
+// lane (r, h) takes row r, K [32h + 8j, +8) for j < 4 and [64 + 32h + 8(j - 4), +8)
+// for j >= 4.
+__device__ __forceinline__ half8_t mma_afrag(const _Float16* abuf, int lane, int rt, int j) {
+  const _Float16* arow = abuf + (lane & 31) * kMmaARow + 32 * (lane >> 5);
+  return *reinterpret_cast<const half8_t*>(arow + rt * 32 * kMmaARow + (j < 4 ? 8 * j : 64 + 8 * (j - 4)));
+}
+
+// The reads of a step's first mma_afrag_ahead() K slices of A fragments,
+// issued before anything else of the step (after the barrier that makes the
+// tile visible), so the first MFMA waits for one LDS round trip only.
+template <int BM, int NTW>
+__device__ __forceinline__ void mma_afrags_first(const _Float16* abuf, int lane, MmaAFrags<BM, NTW>& A) {
+#pragma unroll
+  for (int jj = 0; jj < mma_afrag_ahead<BM, NTW>(); ++jj)
+#pragma unroll
+    for (int rt = 0; rt < BM / 32; ++rt) A[jj][rt] = mma_afrag(abuf, lane, rt, jj);
+}
+
+// One step: the MFMAs of step s, A fragments from the LDS tile (the first
+// slices already requested in A) and B units (converted during the previous
+// step) from registers, in K-slice-major order (slice j: every expert tile
+// t, every row tile rt). The next step's operands are converted during this
+// one, one converted pair (two VALU instructions) at a time: part k of B
+// unit (t, j) right after the k-th MFMA past the last one that reads the
+// unit (from Rn under scale words bswn), the parts of the next step's A
+// chunks spread evenly over the MFMAs, each chunk stored to the other LDS
+// tile after its last part. A wavefront alone on its SIMD issues one
+// instruction every few clocks while an MFMA keeps the matrix core busy for
+// 32, so this even spread (two or three VALU instructions per MFMA at the
+// widest tiles) lets them overlap: with every B unit converted at the top
+// of the step the MFMAs and the conversions ran largely one after the other
+// (large-prefill gate 180 -> 168 us). Scheduling fences keep the order.
+template <int BM, int NTW>
+__device__ __forceinline__ void mma_step(MmaAFrags<BM, NTW>& A, half8_t (&B)[NTW][8],
+                                         const MmaRegs<BM, NTW>& Rn, const uint32_t (&bswn)[NTW][2],
+                                         const uint32_t (&aswn)[mma_row_slots<BM>()], const _Float16* abuf,
+                                         _Float16* abuf_n, int lane,
+                                         f32x16_t (&acc)[mma_sets<BM, NTW>()][BM / 32][NTW]) {
+  constexpr int NS = mma_sets<BM, NTW>();
+  constexpr int SL = mma_row_slots<BM>();
+  constexpr int R = BM / 32;
+  constexpr int NM = R * 8 * NTW;  // MFMAs
+  constexpr int NA = 4 * SL;       // A chunks (units)
+  constexpr int PF = mma_afrag_ahead<BM, NTW>();
+  const int tid = threadIdx.x & (kMmaThreads - 1), q4 = tid & 3;
+  // Scales of the next step, converted after the first MFMA is issued (their
+  // LDS reads went out after the A fragments').
+  half2_t bsc[NTW][2], asc[SL];
+  auto scales = [&]() {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) bsc[t][c] = e4m3x2_f16(bswn[t][c]);
+#pragma unroll
+    for (int i = 0; i < SL; ++i) asc[i] = e4m3x2_f16(aswn[i]);
+  };
+  // Part k of B unit u = (t, j): elements 2k, 2k + 1 of the unit.
+  auto bpart = [&](auto uc) {
+    constexpr int u = decltype(uc)::value, t = u / 32, j = (u / 4) % 8, k = u % 4;
+    const half2_t sc = bsc[t][j / 4];
+    const _Float16 sv = ((j % 4) >> 1) ? sc[1] : sc[0];
+    reinterpret_cast<half2_t*>(&B[t][j])[k] =
+        __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(Rn.b[t][j / 4][j % 4], 1.0f, k) * half2_t{sv, sv};
+  };
+  half2_t Ap[NA][4];
+  auto apart = [&](auto pc) {
+    constexpr int pi = decltype(pc)::value, u = pi / 4, k = pi % 4, i = u / 4, q = u % 4;
+    const half2_t sc = asc[i];
+    const _Float16 sv = (q >> 1) ? sc[1] : sc[0];
+    Ap[u][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(Rn.a[i][q], 1.0f, k) * half2_t{sv, sv};
+    if constexpr (k == 3) {
+      const int row = (tid >> 2) + 64 * i;
+      if (BM >= 64 || row < BM)  // BM = 32: threads 128..255 hold no row
+        reinterpret_cast<half8_t*>(abuf_n + row * kMmaARow + 32 * q4)[q] = half8_t{
+            Ap[u][0][0], Ap[u][0][1], Ap[u][1][0], Ap[u][1][1], Ap[u][2][0], Ap[u][2][1], Ap[u][3][0], Ap[u][3][1]};
+    }
+  };
+  static_for<0, NM>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    constexpr int j = m / (NTW * R), t = (m / R) % NTW, rt = m % R;
+    f32x16_t& c = acc[NS == 2 ? (j >> 2) : 0][rt][t];
+    c = mfma32(A[j % PF][rt], B[t][j], c);
+    if constexpr (m == 0) scales();
+    if constexpr (t == NTW - 1 && j + PF < 8) A[j % PF][rt] = mma_afrag(abuf, lane, rt, j + PF);
+    static_for<0, NTW * 32>([&](auto uc) {
+      constexpr int u = decltype(uc)::value, tt = u / 32, jj = (u / 4) % 8, k = u % 4;
+      constexpr int last = jj * NTW * R + tt * R + R - 1;  // the unit's last MFMA in this step
+      constexpr int slot = last + 1 + k < NM ? last + 1 + k : NM - 1;
+      if constexpr (slot == m) bpart(uc);
+    });
+    static_for<(m * 4 * NA + NM - 1) / NM, ((m + 1) * 4 * NA + NM - 1) / NM>(apart);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
 
 // The K loop of one workgroup tile: KS K groups of four wavefronts (group
 // grp takes K steps grp, grp + KS, ...), loads RING steps ahead in a register
 // ring, A converted into the group's two LDS tiles (abuf + (2 grp + i) BM
-// kMmaARow halves), B converted in registers. One iteration covers a scale
-// window of kMmaWin steps (kMmaWin / (KS RING) ring passes); nsteps is
-// padded to a multiple of it, and padding steps load nothing (k >= D) and
-// add zeros. STAGED: the next window's scale loads are spread over the
-// first half of the window's positions (a position is one step of each
-// group, ending at a barrier) and their LDS stores over the next ones, all
-// before the barrier ahead of the last position, whose A conversion (for
-// the next window's first steps) reads them. swin holds mma_win_bytes()
+// kMmaARow halves), B converted in registers, each during the group's step
+// before the one that uses them. One iteration covers a scale window of
+// kMmaWin steps (kMmaWin / (KS RING) ring passes); nsteps is padded to a
+// multiple of it, and padding steps load nothing (k >= D) and add zeros.
+// STAGED: the next window's scale loads are spread over the first half of
+// the window's positions (a position is one step of each group, ending at a
+// barrier) and their LDS stores over the next ones, all before the barrier
+// ahead of the last position, whose conversions (for the next window's
+// first steps) read them. swin holds mma_win_bytes()
 // bytes. Leaves acc[0] holding this group's sums (the two accumulator sets
 // added).
 template <int BM, int NTW, int KS, bool STAGED>
@@ -387,17 +444,25 @@ __device__ __forceinline__ void mma_mainloop(const MmaPtrs<BM, NTW>& P, int D, i
 #pragma unroll
   for (int p = 0; p < RING; ++p) mma_load<STAGED, BM, NTW>(R[p], P, D, KS * p + grp);
   ScaleWin<BM, NTW, KS> win;
-  uint32_t aw[SL];
+  uint32_t aw[SL], bw[NTW][2];
   if constexpr (STAGED) {
     static_for<0, ScaleWin<BM, NTW, KS>::NL>([&](auto jc) { win.template load<decltype(jc)::value>(P, 0, rows); });
     static_for<0, ScaleWin<BM, NTW, KS>::NL>([&](auto jc) { win.template store<decltype(jc)::value>(swin); });
     __syncthreads();
     a_words(0, grp, aw);
+    b_words(0, grp, bw);
   } else {
 #pragma unroll
     for (int i = 0; i < SL; ++i) aw[i] = R[0].as[i];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) bw[t][c] = R[0].bs[t][c];
   }
+  // The group's first step: A into its first LDS tile, B into registers.
+  half8_t B[NTW][8];
   mma_store_a<BM, NTW>(R[0], aw, abuf(0));
+  mma_convert_b<BM, NTW>(B, R[0], bw);
   __syncthreads();
   for (int s0 = 0; s0 < nsteps; s0 += kMmaWin) {
     const int wi = s0 / kMmaWin, wb = wi & 1;
@@ -405,30 +470,39 @@ __device__ __forceinline__ void mma_mainloop(const MmaPtrs<BM, NTW>& P, int D, i
       constexpr int it = decltype(ic)::value;
       static_for<0, RING>([&](auto pc) {
         constexpr int p = decltype(pc)::value, pos = it * RING + p;
-        // Step s0 + it SPI + KS p + grp: A from tile pos & 1, B from R[p];
-        // the group's next step's A (R[(p + 1) % RING]) into the other
-        // tile; then R[p] (fully used) reloads the step RING ahead.
+        // Step s0 + it SPI + KS p + grp: its A (converted during the step
+        // before) is in tile pos & 1 and its B in registers, so R[p] is
+        // free: it reloads the step RING ahead first. The group's next step
+        // (R[(p + 1) % RING]) is converted during this one: A into the
+        // other tile, B into the registers as this step is done with them.
         constexpr int sw = it * SPI + KS * p;  // step in window, less grp
-        uint32_t bw[NTW][2], an[SL];
+        uint32_t bn[NTW][2], an[SL];
+        MmaAFrags<BM, NTW> A;
+        mma_afrags_first<BM, NTW>(abuf(pos & 1), lane, A);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_load<STAGED, BM, NTW>(R[p], P, D, s0 + it * SPI + KS * (p + RING) + grp);
         if constexpr (STAGED) {
           constexpr int NL = ScaleWin<BM, NTW, KS>::NL, NLP = POS / 2;
           if constexpr (pos < NLP)
             static_for<pos * NL / NLP, (pos + 1) * NL / NLP>(
                 [&](auto jc) { win.template load<decltype(jc)::value>(P, wi + 1, rows); });
-          b_words(wb, sw + grp, bw);
           // The next step is the next window's when sw + KS reaches kMmaWin.
-          if constexpr (sw + KS < kMmaWin) a_words(wb, sw + KS + grp, an);
-          else a_words(wb ^ 1, sw + KS - kMmaWin + grp, an);
+          if constexpr (sw + KS < kMmaWin) {
+            a_words(wb, sw + KS + grp, an);
+            b_words(wb, sw + KS + grp, bn);
+          } else {
+            a_words(wb ^ 1, sw + KS - kMmaWin + grp, an);
+            b_words(wb ^ 1, sw + KS - kMmaWin + grp, bn);
+          }
         } else {
 #pragma unroll
           for (int t = 0; t < NTW; ++t)
 #pragma unroll
-            for (int c = 0; c < 2; ++c) bw[t][c] = R[p].bs[t][c];
+            for (int c = 0; c < 2; ++c) bn[t][c] = R[(p + 1) % RING].bs[t][c];
 #pragma unroll
           for (int i = 0; i < SL; ++i) an[i] = R[(p + 1) % RING].as[i];
         }
-        mma_step<BM, NTW>(R[p], bw, abuf(pos & 1), R[(p + 1) % RING], an, abuf((pos + 1) & 1), lane, acc);
-        mma_load<STAGED, BM, NTW>(R[p], P, D, s0 + it * SPI + KS * (p + RING) + grp);
+        mma_step<BM, NTW>(A, B, R[(p + 1) % RING], bn, an, abuf(pos & 1), abuf((pos + 1) & 1), lane, acc);
         if constexpr (STAGED) {
           constexpr int NL = ScaleWin<BM, NTW, KS>::NL, NSP = POS - 1 - POS / 2;
           if constexpr (pos >= POS / 2 && pos < POS - 1)
