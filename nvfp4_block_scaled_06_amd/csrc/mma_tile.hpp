@@ -268,11 +268,13 @@ constexpr int mma_ksplit() {
 }
 
 // Look-ahead of the A-fragment reads, in K slices (8 per step): one, each
-// fragment read right after the last MFMA that uses its register (the
-// (NTW - 1) BM / 32 MFMAs in between cover the LDS latency at the wide
-// tiles, the other wavefront on the SIMD does at the narrow ones). Measured
-// against two slices ahead: large-prefill gate 171 -> 160 us (fewer
-// registers held), prefill unchanged.
+// fragment read right after the last MFMA that uses its register (with the
+// row tiles outermost in a slice that leaves (BM / 32 - 1) NTW MFMAs to
+// cover the LDS latency at the wide tiles; the other wavefront on the SIMD
+// covers it at the narrow ones). Measured against two slices ahead:
+// large-prefill gate 171 -> 160 us (fewer registers held), prefill
+// unchanged; row tiles outermost instead of innermost and B parts three
+// MFMAs apart: 165.6 -> 160.1 us, prefill 49.2 -> 47.5.
 template <int BM, int NTW>
 constexpr int mma_afrag_ahead() {
   return 1;
@@ -317,11 +319,13 @@ __device__ __forceinline__ void mma_afrags_first(const _Float16* abuf, int lane,
 
 // One step: the MFMAs of step s, A fragments from the LDS tile (the first
 // slices already requested in A) and B units (converted during the previous
-// step) from registers, in K-slice-major order (slice j: every expert tile
-// t, every row tile rt). The next step's operands are converted during this
-// one, one converted pair (two VALU instructions) at a time: part k of B
-// unit (t, j) right after the k-th MFMA past the last one that reads the
-// unit (from Rn under scale words bswn), the parts of the next step's A
+// step) from registers, in K-slice-major order (slice j: every row tile rt,
+// and for each every expert tile t), so an A fragment's register is free
+// after NTW MFMAs and the next slice's fragment is read R NTW - NTW MFMAs
+// before its use. The next step's operands are converted during this one,
+// one converted pair (two VALU instructions) at a time: part k of B unit
+// (t, j) after the (3k + 1)-th MFMA past the last one that reads the unit
+// (from Rn under scale words bswn), the parts of the next step's A
 // chunks spread evenly over the MFMAs, each chunk stored to the other LDS
 // tile after its last part. A wavefront alone on its SIMD issues one
 // instruction every few clocks while an MFMA keeps the matrix core busy for
@@ -376,15 +380,16 @@ __device__ __forceinline__ void mma_step(MmaAFrags<BM, NTW>& A, half8_t (&B)[NTW
   };
   static_for<0, NM>([&](auto mc) {
     constexpr int m = decltype(mc)::value;
-    constexpr int j = m / (NTW * R), t = (m / R) % NTW, rt = m % R;
+    constexpr int j = m / (NTW * R), rt = (m / NTW) % R, t = m % NTW;
     f32x16_t& c = acc[NS == 2 ? (j >> 2) : 0][rt][t];
     c = mfma32(A[j % PF][rt], B[t][j], c);
     if constexpr (m == 0) scales();
     if constexpr (t == NTW - 1 && j + PF < 8) A[j % PF][rt] = mma_afrag(abuf, lane, rt, j + PF);
     static_for<0, NTW * 32>([&](auto uc) {
       constexpr int u = decltype(uc)::value, tt = u / 32, jj = (u / 4) % 8, k = u % 4;
-      constexpr int last = jj * NTW * R + tt * R + R - 1;  // the unit's last MFMA in this step
-      constexpr int slot = last + 1 + k < NM ? last + 1 + k : NM - 1;
+      constexpr int last = jj * NTW * R + (R - 1) * NTW + tt;  // the unit's last MFMA in this step
+      constexpr int want = last + 1 + 3 * k;
+      constexpr int slot = want < NM ? want : NM - 1;
       if constexpr (slot == m) bpart(uc);
     });
     static_for<(m * 4 * NA + NM - 1) / NM, ((m + 1) * 4 * NA + NM - 1) / NM>(apart);
