@@ -171,17 +171,45 @@ __device__ __forceinline__ void row16_route(const float* const (&Lrow)[NSET], co
   for (int j4 = 0; j4 < J16 / 4; ++j4) {
     const float4 B4 = *reinterpret_cast<const float4*>(bias_lds + e0 + 4 * j4);
     const float Bv[4] = {B4.x, B4.y, B4.z, B4.w};
+    // The 4 NSET keys of this group of experts, one stage at a time (the
+    // operations of sigmoid_fast, then the bias and the key): each stage's
+    // results are pinned before the next starts, so the independent chains
+    // interleave; left to itself the compiler runs each key's chain to the
+    // end through one register, and with one wavefront per SIMD every
+    // dependent step (two transcendentals among them) then waits. Every
+    // lane computes every key, masked afterwards (inside the select the
+    // sigmoid was sunk into a branch per key).
+    float v[NSET][4];
 #pragma unroll
     for (int r = 0; r < NSET; ++r) {
       const float4 L4 = *reinterpret_cast<const float4*>(Lrow[r] + e0 + 4 * j4);
-      const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
+      v[r][0] = L4.x;
+      v[r][1] = L4.y;
+      v[r][2] = L4.z;
+      v[r][3] = L4.w;
+    }
+    auto pin = [&]() {
+#pragma unroll
+      for (int r = 0; r < NSET; ++r) asm volatile("" : "+v"(v[r][0]), "+v"(v[r][1]), "+v"(v[r][2]), "+v"(v[r][3]));
+    };
+    auto stage = [&](auto f) {
+#pragma unroll
+      for (int r = 0; r < NSET; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[r][i] = f(v[r][i], i);
+      pin();
+    };
+    stage([](float x, int) { return __builtin_amdgcn_exp2f(-1.4426950408889634f * x); });
+    stage([](float x, int) { return __builtin_amdgcn_rcpf(1.0f + x); });  // = sigmoid_fast(L)
+    stage([&](float x, int i) { return x + Bv[i]; });
+#pragma unroll
+    for (int r = 0; r < NSET; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 4 * j4 + i;
-        key[r][j] = (e0 + j < E && valid[r]) ? sum_key(sigmoid_fast(Lv[i]) + Bv[i]) : 0u;
+        key[r][j] = (e0 + j < E && valid[r]) ? sum_key(v[r][i]) : 0u;
         lm[r] = max(lm[r], key[r][j]);
       }
-    }
   }
   // Survivors: the keys above hi (never key 0, as hi >= 0). The bound: hi =
   // tau - 1; the exact search: hi = K - 1, after zeroing the keys equal to K
