@@ -41,9 +41,11 @@ struct TileArgs {
 //    [32h + 8j, +8) for j < 4 and [64 + 32h + 8(j - 4), +8) for j >= 4, on A
 //    and on B alike, so every product meets its partner and each K value is
 //    used once.
-//  * Loads run mma_ring() steps ahead in a register ring.
+//  * Loads run mma_ring() steps ahead in a register ring; both operands of a
+//    step are converted during the step before it, between its MFMAs.
 //  * Epilogue: when the tile holds every expert, scaled accumulators go
-//    through LDS, 32 tokens at a time, into the 16-lanes-per-token router.
+//    through LDS, 32 or 64 tokens at a time, into the 16-lanes-per-token
+//    router.
 //    When E is split over NCB workgroups, each stores its logits to the
 //    workspace (device-coherent) and the last of the token block's NCB
 //    workgroups to arrive loads them all and routes the block.

@@ -11,6 +11,8 @@
 //  * B (columns): each lane loads two 32-element chunks of its column row
 //    per step (16 code bytes + 2 scale bytes each) and converts them in
 //    registers; no other wavefront needs them.
+//  * Both operands of a step are converted during the step before it,
+//    spread evenly between that step's MFMAs (mma_step).
 //  * K permutation: lane (r, h) of a 32x32x16 MFMA supplies 8 K values of
 //    row/column r from group h; in step-relative K, MFMA j (0..7) takes
 //    [32h + 8j, +8) for j < 4 and [64 + 32h + 8(j - 4), +8) for j >= 4, on A
