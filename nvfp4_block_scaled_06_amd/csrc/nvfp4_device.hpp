@@ -146,12 +146,13 @@ __device__ __forceinline__ uint32_t fp4_exact8(const uint32_t* w, float inv, flo
 // are not decided here: callers screen them out with near_scale_key). Normal
 // range: round the fp32 pattern to 3 mantissa bits (the carry rolls into the
 // exponent) and rebias 127 -> 7; subnormal range (p < 2^-6): p * 2^9 rounded.
+// Both roundings are formed and one is selected (no branch: blocks of one
+// wavefront often mix normal and subnormal scales).
 __device__ __forceinline__ uint32_t e4m3_from_f32(float p) {
-  if (p >= 0x1p-6f) {
-    const uint32_t u = __float_as_uint(p);
-    return ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
-  }
-  return (uint32_t)rintf(p * 512.0f);
+  const uint32_t u = __float_as_uint(p);
+  const uint32_t normal = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+  const uint32_t subnormal = (uint32_t)rintf(p * 512.0f);
+  return p >= 0x1p-6f ? normal : subnormal;
 }
 
 // Distance key to the nearest value with at most four explicit mantissa bits
