@@ -114,12 +114,23 @@ __device__ __forceinline__ void route_tile(const TileArgs& a, int ncb, int rb, i
       tile_to_lds(rtc, 0);
       __syncthreads();
       const int nrows = min(32, a.T - base);
-      for (int i = threadIdx.x; i < 32 * 128 * NTW; i += kMmaThreads * KS) {
-        const int mm = i / (128 * NTW), c = i - mm * (128 * NTW), e = col0 + c;
+      // Every LDS read of the pass first, then the stores: one element per
+      // loop trip waited for each read in turn.
+      constexpr int PER = 32 * 128 * NTW / (kMmaThreads * KS);  // elements per thread
+      static_assert(32 * 128 * NTW % (kMmaThreads * KS) == 0, "whole elements per thread");
+      float L[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int i = threadIdx.x + u * kMmaThreads * KS, mm = i / (128 * NTW), c = i - mm * (128 * NTW);
+        L[u] = lg[mm * ldE + c];
+      }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int i = threadIdx.x + u * kMmaThreads * KS, mm = i / (128 * NTW), c = i - mm * (128 * NTW);
+        const int e = col0 + c;
         if (mm < nrows && e < E) {
-          const float L = lg[mm * ldE + c];
-          store_coherent(a.lbuf + (int64_t)(base + mm) * E + e, L);
-          if (a.logits_out) a.logits_out[(int64_t)(base + mm) * E + e] = L;
+          store_coherent(a.lbuf + (int64_t)(base + mm) * E + e, L[u]);
+          if (a.logits_out) a.logits_out[(int64_t)(base + mm) * E + e] = L[u];
         }
       }
     };
