@@ -223,9 +223,15 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t D, const float* 
     if (err != hipSuccess) return err;
   }
   // Equal grid-stride passes for every thread: a last pass that only part of
-  // the threads take would cost the whole VALU issue of one.
+  // the threads take would cost the whole VALU issue of one. When x is small
+  // enough to be re-read from the Infinity Cache, half the workgroups (each
+  // folding the partial maxima once and taking twice the blocks) measured
+  // faster (T = 8192, D = 7168: 49.0-49.6 -> 47.1-47.4 us); streaming x from
+  // HBM, the full grid keeps more loads in flight (T = 32768: 191 against
+  // 196 us with half).
+  const int64_t max_grid = nblocks * 32 <= kAmaxCachedBytes ? kQuantMaxGrid / 2 : kQuantMaxGrid;
   const int64_t want = (nblocks + kQuantThreads - 1) / kQuantThreads;
-  const int64_t passes = (want + kQuantMaxGrid - 1) / kQuantMaxGrid;
+  const int64_t passes = (want + max_grid - 1) / max_grid;
   const int grid = (int)((want + passes - 1) / passes);
   quant_kernel<<<grid, kQuantThreads, 0, stream>>>(xv, nblocks, partial, npartial, gsa_override, cv, scales,
                                                    gsa_out);
