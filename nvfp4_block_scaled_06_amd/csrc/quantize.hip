@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const u32x4_
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
-constexpr int kQuantThreads = 256;
+constexpr int kQuantThreads = 512;
 
 __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const u32x4_t* __restrict__ x, int64_t nblocks,
                                                               const uint32_t* __restrict__ partial, int npartial,
@@ -223,13 +223,14 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t D, const float* 
     if (err != hipSuccess) return err;
   }
   // Equal grid-stride passes for every thread: a last pass that only part of
-  // the threads take would cost the whole VALU issue of one. When x is small
-  // enough to be re-read from the Infinity Cache, half the workgroups (each
-  // folding the partial maxima once and taking twice the blocks) measured
-  // faster (T = 8192, D = 7168: 49.0-49.6 -> 47.1-47.4 us); streaming x from
-  // HBM, the full grid keeps more loads in flight (T = 32768: 191 against
-  // 196 us with half).
-  const int64_t max_grid = nblocks * 32 <= kAmaxCachedBytes ? kQuantMaxGrid / 2 : kQuantMaxGrid;
+  // the threads take would cost the whole VALU issue of one. Workgroups of
+  // 512 threads, each folding the partial maxima once. When x is small enough
+  // to be re-read from the Infinity Cache, at most 2048 of them (four blocks
+  // per thread at T = 8192, D = 7168: 48.7-49.6 us with 7168 workgroups of
+  // 256, 47.1-47.4 with 3584, 46.3-47.2 with 1792 of 512); streaming x from
+  // HBM, up to 8192 keep more loads in flight (T = 32768: 186.0-187.9 us
+  // against 189.2-190.5 with 8192 of 256, 188.7-189.6 with 4096 of 512).
+  const int64_t max_grid = nblocks * 32 <= kAmaxCachedBytes ? kQuantMaxGrid / 4 : kQuantMaxGrid;
   const int64_t want = (nblocks + kQuantThreads - 1) / kQuantThreads;
   const int64_t passes = (want + max_grid - 1) / max_grid;
   const int grid = (int)((want + passes - 1) / passes);
