@@ -116,7 +116,11 @@ __global__ __launch_bounds__(kSingleThreads) void quant_single_kernel(const u32x
 }
 
 constexpr int kAmaxThreads = 256;
-constexpr int kAmaxUnroll = 4;
+// Loads in flight per thread in the max pass: two measured best (amax +
+// quantize at T = 8192, D = 7168: 45.5-45.7 us against 46.2-46.5 with four
+// and one; at T = 32768, streaming: 181.4-181.7 against 185.0 with three,
+// 187.8-189.5 with four or one, 203 with eight).
+constexpr int kAmaxUnroll = 2;
 
 // Tensors up to this size are read by the max pass with ordinary loads, so
 // that they stay in the 256 MB Infinity Cache for the quantize pass; larger
