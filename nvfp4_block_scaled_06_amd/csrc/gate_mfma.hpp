@@ -62,13 +62,16 @@ struct MmaArgs {
 // Epilogue rows per pass: 64 when the tile has them and their logits rows
 // fit the LDS (up to 384 experts), else 32 (fewer passes: measured 2-3 %
 // of the large-prefill gate with one K group). Each wavefront routes
-// LR / (4 KS) rows per pass, as sets of four, two sets per call
-// (interleaved, for latency hiding: with one wavefront per SIMD this was
-// worth ~6 % of the large-prefill gate).
+// LR / (4 KS) rows per pass, as sets of four. One K group: two sets per
+// call (interleaved, for latency hiding: with one wavefront per SIMD this
+// was worth ~6 % of the large-prefill gate). Two K groups: one set per call,
+// the SIMD's other wavefront hiding the latency (the prefill gate at
+// T = 8192, E = 256: 47.2-47.8 -> 46.2-46.9 us against two sets, same run,
+// bit-identical outputs).
 template <int BM, int J16, int KS>
 constexpr int epi_rows() { return BM >= 64 && J16 <= 24 ? 64 : 32; }
 template <int BM, int J16, int KS>
-constexpr int epi_sets() { return KS == 2 ? epi_rows<BM, J16, KS>() / 32 : 2; }
+constexpr int epi_sets() { return KS == 2 ? 1 : 2; }
 
 // LDS row stride of the epilogue's logits, in floats: the router reads 16 J16
 // entries per row (16 bytes at a time), and the accumulators of a whole
