@@ -112,7 +112,9 @@ __global__ __launch_bounds__(kMmaThreads * KS) __attribute__((amdgpu_waves_per_e
 // stream of the packed expert weights, so it takes the lm_head GEMV's
 // shape rather than MFMA tiles (which would multiply mostly zero rows).
 // Workgroup (g, column tile) = 64 weight rows of group g, four wavefronts
-// of 16 rows with 4 rows' loads in flight; lane l takes the 32-element
+// of 16 rows with 2 rows' loads in flight (as in the lm_head GEMV; GEMM
+// 24.2-24.8 against 25.8-26.1 us with 4, 28.5-30.0 with 1, at G = 8, N =
+// 4096, D = 7168); lane l takes the 32-element
 // chunks l, l + 64, ... of a row (coalesced 1 KB per wavefront load,
 // nontemporal: every weight byte is read once). The group's rows of x are
 // converted once per workgroup into LDS as exact fp16 q S values; block
@@ -122,7 +124,7 @@ constexpr int kGvWaves = 4;
 constexpr int kGvThreads = 64 * kGvWaves;
 constexpr int kGvRowsPerWave = 16;
 constexpr int kGvCols = kGvWaves * kGvRowsPerWave;  // weight rows (output columns) per workgroup
-constexpr int kGvInFlight = 4;
+constexpr int kGvInFlight = 2;
 constexpr int kGvMaxRows = 4;
 constexpr int kGvMaxXHalves = 32768;  // rows x D of the fp16 x copy in LDS (64 KB)
 

@@ -9,10 +9,12 @@
 // bandwidth: the same GEMV design as the router's decode gate at a size where
 // the bandwidth, not the launch and handoff latency, sets the time.
 //
-//  * Workgroup: 64 rows, four wavefronts of 16 rows, 4 rows in flight per
+//  * Workgroup: 64 rows, four wavefronts of 16 rows, 2 rows in flight per
 //    wavefront at all times (a rolling ring: a row's loads are issued as soon
-//    as the row four before it is summed); lane l takes the 32-element chunks
-//    l, l + 64, ... of a row (16 code bytes and 2 scale bytes each, coalesced
+//    as the row two before it is summed; two measured faster than one,
+//    three or four: 89.9-92.6 against 94.9-96.7 us per call with four at
+//    N = 129280, D = 7168); lane l takes the 32-element chunks l, l + 64,
+//    ... of a row (16 code bytes and 2 scale bytes each, coalesced
 //    1 KB per wavefront).
 //    The weights are read once per call, with nontemporal loads (measured:
 //    110 us against 115 us with cached loads at 129,280 x 7168; 8 rows in
@@ -33,7 +35,7 @@ constexpr int kLmWaves = 4;
 constexpr int kLmThreads = 64 * kLmWaves;
 constexpr int kLmRowsPerWave = 16;
 constexpr int kLmRows = kLmWaves * kLmRowsPerWave;  // rows per workgroup
-constexpr int kLmInFlight = 4;                       // rows per wavefront whose loads are issued together
+constexpr int kLmInFlight = 2;                       // rows per wavefront whose loads are in flight
 constexpr int kLmMaxT = 4;
 constexpr int kLmMaxD = 16384;
 
